@@ -1,0 +1,182 @@
+/*
+ * bitdelta.h — C ABI of the MI355X (gfx950) BitDelta hot path.
+ *
+ * Method: the hanzo blog post "BitDelta: serving 14 Zen models from one GPU cluster"
+ * (2026-02-28; "the BitDelta post" below).  A fine-tuned variant of a base model is stored per
+ * weight matrix as one float32 scale alpha = mean|Delta| and one sign bit per element
+ * ("The mathematical foundation"); at serving time each token's output is
+ * y = x * (W_base + alpha_v * sign(Delta_v))^T for the variant v the token's request names,
+ * computed without ever writing W_base + alpha_v * sign(Delta_v) to memory ("Serving
+ * architecture": reconstruction fused with the multiply).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked [dev] are device (HBM) pointers; [host] are host pointers.
+ *   - The caller owns every buffer.  The library never allocates device memory, keeps no
+ *     state between calls, and is safe to call from several host threads.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *     A call returns as soon as its kernels are enqueued.
+ *   - Argument errors are detected on the host BEFORE anything is enqueued and are reported
+ *     as a status; no device memory is touched in that case.  Launch failures report
+ *     BITDELTA_ERR_HIP.
+ *   - Sign bits: element (r, k) of a d_out x d_in matrix is bit (k % 32) of the uint32 word
+ *     r * (d_in / 32) + k / 32, least-significant bit first; bit 1 means +1, bit 0 means -1.
+ *     The byte image of these words equals the BitDelta post's packing of eight sign bits per
+ *     int8 ("Infrastructure details", delta storage format).  sign(+0) = sign(-0) = +1.
+ *   - bf16 tensors are passed as `const void*` holding IEEE bfloat16 values, row-major.
+ *   - d_in must be a multiple of 32 (one word per 32 elements of a row).
+ */
+#ifndef BITDELTA_H_
+#define BITDELTA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITDELTA_ABI_VERSION 1
+#define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
+#define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
+#define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
+
+typedef enum {
+  BITDELTA_OK = 0,
+  BITDELTA_ERR_INVALID_ARG = 1, /* null pointer, negative size, unknown enum value            */
+  BITDELTA_ERR_SHAPE = 2,       /* d_in not a multiple of 32, inconsistent segments           */
+  BITDELTA_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned (words: 4-byte)    */
+  BITDELTA_ERR_WORKSPACE = 4,   /* workspace smaller than bitdelta_compress_workspace_bytes   */
+  BITDELTA_ERR_UNSUPPORTED = 5, /* a size beyond what the kernels handle                      */
+  BITDELTA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing         */
+} bitdelta_status;
+
+typedef void* bitdelta_stream; /* hipStream_t */
+
+typedef enum { BITDELTA_OUT_BF16 = 0, BITDELTA_OUT_F32 = 1 } bitdelta_out_dtype;
+
+/* Which kernel family runs a matmul.  AUTO picks by batch shape; the others force one (for
+ * tests and measurement).  Every path computes the same y within the documented tolerance. */
+typedef enum {
+  BITDELTA_PATH_AUTO = 0,
+  BITDELTA_PATH_GEMV = 1,    /* fp32 reconstruction in registers, VALU; M <= 4                 */
+  BITDELTA_PATH_STREAM = 2,  /* decode: split base/sign bf16 MFMA, each weight byte read once  */
+  BITDELTA_PATH_PREFILL = 3  /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
+} bitdelta_path;
+
+/* One compressed variant of one weight matrix: the output of bitdelta_compress. */
+typedef struct {
+  const uint32_t* sign_words; /* [dev] d_out * d_in / 32 words, layout above, 4-byte aligned */
+  const float* alpha;         /* [dev] one float32: the per-matrix scale                      */
+} bitdelta_variant;
+
+/* One linear layer of a grouped matmul: every problem of a call sees the same token batch
+ * segmentation (same M, same segments), with its own activations, weights and variants. */
+typedef struct {
+  const void* x;                    /* [dev] bf16 [M][d_in], rows in segment order, 16B-aligned */
+  const void* w_base;               /* [dev] bf16 [d_out][d_in], 16-byte aligned                */
+  void* y;                          /* [dev] [M][d_out] bf16 or f32 (y_dtype), 16-byte aligned  */
+  int64_t d_out;
+  int64_t d_in;                     /* multiple of 32                                           */
+  const bitdelta_variant* variants; /* [host] num_variants entries (may be NULL if 0)           */
+  int32_t num_variants;
+} bitdelta_problem;
+
+/* ABI version of the loaded library (BITDELTA_ABI_VERSION). */
+int bitdelta_abi_version(void);
+
+/* Static string naming a status code. */
+const char* bitdelta_status_string(int status);
+
+/* Number of uint32 sign words of a d_out x d_in matrix (d_out * d_in / 32), or -1 if d_in is
+ * not a positive multiple of 32 or d_out is negative. */
+int64_t bitdelta_sign_words(int64_t d_out, int64_t d_in);
+
+/* Device workspace bytes bitdelta_compress needs for this shape (fp64 partial sums). */
+size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
+
+/*
+ * bitdelta_compress — the compression step of the BitDelta post ("The mathematical
+ * foundation"): alpha = ||Delta||_1 / n, the mean absolute value over all n = d_out * d_in
+ * elements (exact zeros included), and sign(Delta) packed one bit per element.
+ *
+ *   delta       [dev] float32 [d_out][d_in], 16-byte aligned, finite values.  Read only.
+ *   sign_words  [dev] out: uint32 [d_out][d_in/32] (layout above), 4-byte aligned.
+ *   alpha       [dev] out: one float32, the fp64 sum of |Delta| (fixed summation order, so
+ *               repeated calls are bit-identical) divided by n and rounded once to float32.
+ *   workspace   [dev] at least bitdelta_compress_workspace_bytes(d_out, d_in) bytes,
+ *               8-byte aligned; scratch only, contents on return unspecified.
+ * Errors: INVALID_ARG (null pointer, d_out <= 0), SHAPE (d_in not a positive multiple of 32),
+ * ALIGNMENT, WORKSPACE (workspace_bytes too small), HIP.
+ * The buffers must not overlap.
+ */
+bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
+                                  uint32_t* sign_words, float* alpha, void* workspace,
+                                  size_t workspace_bytes, bitdelta_stream stream);
+
+/*
+ * bitdelta_plan_segments — group a token batch by variant (host only, O(M), no device work).
+ * The BitDelta post's router sends each request to its variant while the base weights are one
+ * shared read ("Serving architecture"); this groups tokens so one matmul call serves them all.
+ * Stable counting sort by variant id: the base model (-1) first, then 0..num_variants-1;
+ * empty groups are dropped.
+ *
+ *   token_variant [host] int32 [M], each in [-1, num_variants).
+ *   perm          [host] out int32 [M]: sorted position p holds original token perm[p].
+ *   seg_offsets   [host] out int32 [num_variants + 2]: segment s covers sorted positions
+ *                 [seg_offsets[s], seg_offsets[s+1]); seg_offsets[0] = 0.
+ *   seg_variant   [host] out int32 [num_variants + 1]: variant of segment s (-1 = base).
+ *   num_segments  [host] out: number of non-empty segments.
+ * Errors: INVALID_ARG (null pointer, M < 0, num_variants outside [0, BITDELTA_MAX_VARIANTS],
+ * a variant id out of range; nothing is written then).  M = 0 yields zero segments.
+ */
+bitdelta_status bitdelta_plan_segments(const int32_t* token_variant, int64_t M,
+                                       int32_t num_variants, int32_t* perm,
+                                       int32_t* seg_offsets, int32_t* seg_variant,
+                                       int32_t* num_segments);
+
+/*
+ * bitdelta_matmul — the fused reconstruct-and-multiply of the BitDelta post ("Serving
+ * architecture", conceptual fused linear): for every token t in segment s with variant
+ * v = seg_variant[s],
+ *     y[t][r] = sum_k x[t][k] * (w_base[r][k] + alpha_v * sign_v[r][k])
+ * and for v = -1 (the base model) y[t][r] = sum_k x[t][k] * w_base[r][k].
+ * W_base is read once per call for the whole batch and each variant's bits once; the
+ * reconstructed weight is never written to memory.  Accumulation is fp32.
+ *
+ *   x            [dev] bf16 [M][d_in], rows grouped by segment (see bitdelta_plan_segments).
+ *   w_base       [dev] bf16 [d_out][d_in].
+ *   variants     [host] array of num_variants compressed variants of this matrix.
+ *   seg_offsets  [host] int32 [num_segments + 1], 0 = first <= ... <= last = M.
+ *   seg_variant  [host] int32 [num_segments], each in [-1, num_variants).
+ *   y            [dev] out [M][d_out], bf16 (round-to-nearest-even) or float32 per y_dtype.
+ * M = 0 is a no-op (x and y may then be NULL).  Errors: INVALID_ARG, SHAPE, ALIGNMENT,
+ * UNSUPPORTED, HIP.  y must not alias any input.
+ */
+bitdelta_status bitdelta_matmul(const void* x, const void* w_base, int64_t M, int64_t d_out,
+                                int64_t d_in, const bitdelta_variant* variants,
+                                int32_t num_variants, const int32_t* seg_offsets,
+                                const int32_t* seg_variant, int32_t num_segments, void* y,
+                                int32_t y_dtype, bitdelta_stream stream);
+
+/*
+ * bitdelta_matmul_grouped — bitdelta_matmul over up to BITDELTA_MAX_PROBLEMS independent
+ * linears that share one token segmentation (e.g. the seven linears of a decoder block for
+ * one decode batch), enqueued as few launches as possible so small matrices share the GPU.
+ * `path` selects the kernel family (bitdelta_path); AUTO picks by M and segment sizes.
+ * Errors as bitdelta_matmul, checked for every problem before anything is enqueued.
+ */
+bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_t num_problems,
+                                        int64_t M, const int32_t* seg_offsets,
+                                        const int32_t* seg_variant, int32_t num_segments,
+                                        int32_t y_dtype, int32_t path, bitdelta_stream stream);
+
+/* The kernel family bitdelta_matmul_grouped's AUTO would pick for this batch (a
+ * bitdelta_path value), or -1 for invalid segments.  Host only. */
+int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t* seg_variant,
+                           int32_t num_segments);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITDELTA_H_ */

@@ -1,0 +1,226 @@
+"""Python binding of libbitdelta (the MI355X BitDelta hot path).
+
+Thin ctypes marshalling only: every step of compression and of the fused reconstruct-and-
+multiply runs in the library's HIP kernels.  torch is used to hold device memory and to name
+the current HIP stream.  If the library is not built this module raises on first use; there
+is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "BitDeltaError", "lib", "abi_version", "sign_words", "compress_workspace_bytes",
+    "compress", "plan_segments", "matmul", "matmul_grouped", "auto_path", "PATHS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitdelta.so")
+
+PATHS = {"auto": 0, "gemv": 1, "stream": 2, "prefill": 3}
+_OUT = {"bf16": 0, "f32": 1}
+MAX_VARIANTS = 64
+MAX_PROBLEMS = 8
+
+
+class BitDeltaError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = int(status)
+        name = _lib().bitdelta_status_string(int(status)).decode() if _LIB is not None else str(status)
+        super().__init__(f"{what}: {name} (status {status})" if what else f"{name} (status {status})")
+
+
+class _Variant(ctypes.Structure):
+    _fields_ = [("sign_words", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("w_base", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
+        ("variants", ctypes.POINTER(_Variant)), ("num_variants", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bitdelta_abi_version.restype = ctypes.c_int
+        L.bitdelta_status_string.restype = ctypes.c_char_p
+        L.bitdelta_status_string.argtypes = [ctypes.c_int]
+        L.bitdelta_sign_words.restype = ctypes.c_int64
+        L.bitdelta_sign_words.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.bitdelta_compress_workspace_bytes.restype = ctypes.c_size_t
+        L.bitdelta_compress_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.bitdelta_compress.restype = ctypes.c_int
+        L.bitdelta_compress.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_plan_segments.restype = ctypes.c_int
+        L.bitdelta_plan_segments.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
+                                             _i32p, _i32p]
+        L.bitdelta_matmul.restype = ctypes.c_int
+        L.bitdelta_matmul.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_Variant),
+                                      ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.bitdelta_matmul_grouped.restype = ctypes.c_int
+        L.bitdelta_matmul_grouped.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32,
+                                              ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.bitdelta_auto_path.restype = ctypes.c_int32
+        L.bitdelta_auto_path.argtypes = [ctypes.c_int64, _i32p, _i32p, ctypes.c_int32]
+        _LIB = L
+    return _LIB
+
+
+lib = _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise BitDeltaError(status, what)
+
+
+def _i32(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_i32p)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype_name, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA/HIP torch tensor")
+    if str(t.dtype) != dtype_name:
+        raise TypeError(f"{what} must be {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def abi_version() -> int:
+    return int(_lib().bitdelta_abi_version())
+
+
+def sign_words(d_out: int, d_in: int) -> int:
+    return int(_lib().bitdelta_sign_words(d_out, d_in))
+
+
+def compress_workspace_bytes(d_out: int, d_in: int) -> int:
+    return int(_lib().bitdelta_compress_workspace_bytes(d_out, d_in))
+
+
+def compress(delta, words, alpha, workspace=None, stream=None):
+    """alpha = mean|delta| and packed sign bits of one float32 [d_out, d_in] matrix.
+    ``words``: int32 tensor [d_out, d_in // 32] (uint32 bit patterns), ``alpha``: float32 [1]."""
+    import torch
+    d_out, d_in = delta.shape
+    if workspace is None:
+        workspace = torch.empty(max(compress_workspace_bytes(d_out, d_in), 8) // 8,
+                                dtype=torch.float64, device=delta.device)
+    _check(_lib().bitdelta_compress(
+        _dev(delta, "torch.float32", "delta"), d_out, d_in, _dev(words, "torch.int32", "words"),
+        _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "bitdelta_compress")
+    return words, alpha
+
+
+def plan_segments(token_variant, num_variants: int):
+    """Stable grouping of tokens by variant (base -1 first).  Returns numpy int32
+    (perm, seg_offsets, seg_variant)."""
+    ids, ids_p = _i32(token_variant)
+    m = ids.size
+    perm = np.zeros(max(m, 1), dtype=np.int32)
+    offs = np.zeros(num_variants + 2, dtype=np.int32)
+    segv = np.zeros(num_variants + 1, dtype=np.int32)
+    ns = ctypes.c_int32(0)
+    _check(_lib().bitdelta_plan_segments(
+        ids_p, m, num_variants, perm.ctypes.data_as(_i32p), offs.ctypes.data_as(_i32p),
+        segv.ctypes.data_as(_i32p), ctypes.byref(ns)), "bitdelta_plan_segments")
+    n = ns.value
+    return perm[:m].copy(), offs[:n + 1].copy(), segv[:n].copy()
+
+
+def auto_path(m: int, seg_offsets, seg_variant) -> int:
+    o, op = _i32(seg_offsets)
+    v, vp = _i32(seg_variant)
+    return int(_lib().bitdelta_auto_path(m, op, vp, v.size))
+
+
+def _variants_array(variants):
+    arr = (_Variant * max(len(variants), 1))()
+    for i, item in enumerate(variants):
+        if item is None:
+            continue
+        words, alpha = item
+        arr[i].sign_words = _dev(words, "torch.int32", "sign words")
+        arr[i].alpha = _dev(alpha, "torch.float32", "alpha")
+    return arr
+
+
+def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="auto", stream=None):
+    """Fused y = x (W_base + alpha_v sign_v)^T for several linears sharing one segmentation.
+    ``problems``: list of (x, w_base, y, variants) with variants a list of (words, alpha)."""
+    if not 1 <= len(problems) <= MAX_PROBLEMS:
+        raise ValueError("1..8 problems per call")
+    offs, offs_p = _i32(seg_offsets)
+    segv, segv_p = _i32(seg_variant)
+    m = int(offs[-1]) if offs.size else 0
+    parr = (_Problem * len(problems))()
+    keep = []
+    for i, (x, w, y, variants) in enumerate(problems):
+        varr = _variants_array(variants)
+        keep.append(varr)
+        parr[i].x = _dev(x, "torch.bfloat16", "x")
+        parr[i].w_base = _dev(w, "torch.bfloat16", "w_base")
+        parr[i].y = _dev(y, "torch.bfloat16" if out_dtype == "bf16" else "torch.float32", "y")
+        parr[i].d_out, parr[i].d_in = int(w.shape[0]), int(w.shape[1])
+        parr[i].variants = ctypes.cast(varr, ctypes.POINTER(_Variant))
+        parr[i].num_variants = len(variants)
+        if x.shape[0] != m or y.shape[0] != m:
+            raise ValueError("x and y must have seg_offsets[-1] rows")
+    _check(_lib().bitdelta_matmul_grouped(parr, len(problems), m, offs_p, segv_p, segv.size,
+                                          _OUT[out_dtype], PATHS[path], _stream(stream)),
+           "bitdelta_matmul_grouped")
+    return [p[2] for p in problems]
+
+
+def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf16", path="auto",
+           stream=None):
+    """Fused y = x (W_base + alpha_v sign_v)^T over a token batch grouped by variant."""
+    import torch
+    if y is None:
+        y = torch.empty((x.shape[0], w_base.shape[0]), device=x.device,
+                        dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    if path != "auto":
+        matmul_grouped([(x, w_base, y, variants)], seg_offsets, seg_variant, out_dtype, path,
+                       stream)
+        return y
+    offs, offs_p = _i32(seg_offsets)
+    segv, segv_p = _i32(seg_variant)
+    varr = _variants_array(variants)
+    _check(_lib().bitdelta_matmul(
+        _dev(x, "torch.bfloat16", "x"), _dev(w_base, "torch.bfloat16", "w_base"),
+        int(x.shape[0]), int(w_base.shape[0]), int(w_base.shape[1]), varr, len(variants),
+        offs_p, segv_p, segv.size,
+        _dev(y, "torch.bfloat16" if out_dtype == "bf16" else "torch.float32", "y"),
+        _OUT[out_dtype], _stream(stream)), "bitdelta_matmul")
+    return y

@@ -1,0 +1,98 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of libbitdelta.
+// Nothing here is part of the public ABI (include/bitdelta.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------------------------
+// bf16 <-> f32 helpers (bf16 is the upper half of an IEEE binary32).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo_to_f32(unsigned pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(unsigned pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Round-to-nearest-even f32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Compress (two passes)
+// ---------------------------------------------------------------------------------------------
+int compress_grid(int64_t n);  // number of pass-1 workgroups (= fp64 partials) for n elements
+hipError_t launch_compress(const float* delta, int64_t n, uint32_t* words, float* alpha,
+                           double* partials, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Matmul kernels
+// ---------------------------------------------------------------------------------------------
+constexpr int kMaxSlots = 16;     // distinct variants one streaming launch serves
+constexpr int kMaxProblems = 8;   // linears one streaming launch serves
+
+// GEMV (M <= 4): one launch per linear.
+struct GemvArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  void* y;
+  int d_out, d_in, M, y_f32;
+  // per token: the variant slot (-1 = base) and whether it differs from the previous token
+  int tok_slot[4];
+  const uint32_t* words[4];
+  const float* alpha[4];
+};
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+
+// Streaming decode: token tiles of 16 rows, each tile within one segment.
+constexpr int kStreamMaxTiles = 24;
+constexpr int kStreamMaxM = 256;
+constexpr int kStreamRowsPerBlock = 64;
+
+struct StreamProblem {
+  const uint16_t* x;
+  const uint16_t* w;
+  void* y;
+  int d_out, d_in;
+  int block_begin;
+  int pad_;
+  const uint32_t* words[kMaxSlots];
+  const float* alpha[kMaxSlots];
+};
+
+struct StreamArgs {
+  StreamProblem prob[kMaxProblems];
+  int nprob, ntiles, nslots, M, y_f32, pad_;
+  int8_t tile_slot[kStreamMaxTiles];   // slot of the tile's variant, -1 for the base model
+  uint8_t tile_valid[kStreamMaxTiles]; // rows of the tile that are real tokens (1..16)
+  int16_t tile_src[kStreamMaxTiles];   // first x row of the tile
+};
+hipError_t launch_stream(const StreamArgs& a, int nblocks, hipStream_t stream);
+
+// Prefill: per-segment tiles of 256 tokens x 128 output rows, W_eff rebuilt in LDS.
+constexpr int kPrefillBM = 256;
+constexpr int kPrefillBN = 128;
+constexpr int kPrefillMaxMTiles = 256;
+
+struct PrefillArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  void* y;
+  int d_out, d_in, y_f32, n_mtiles, n_ntiles, pad_;
+  const uint32_t* words[kMaxSlots];
+  const float* alpha[kMaxSlots];
+  // per M-tile: first x row, rows in the tile (1..256), variant slot (-1 = base)
+  int mt_row[kPrefillMaxMTiles];
+  int16_t mt_rows[kPrefillMaxMTiles];
+  int8_t mt_slot[kPrefillMaxMTiles];
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace bd

@@ -1,0 +1,70 @@
+"""Shared helpers of the GPU parity tests: moving seeded inputs to the device, running the
+library through its C ABI, and the error metrics the tolerances are stated in."""
+import numpy as np
+
+import oracle.bitdelta_oracle as O
+
+# Per token row of y: ||y_gpu - y_ref||_2 / ||y_ref||_2 (fp64 oracle); the stated bound.
+ROW_L2_TOL = 2e-2
+# bf16 output: the error must stay well below the size of the delta term itself, so a kernel
+# that dropped or flipped the delta (ratio ~1 or ~2) cannot pass.
+DELTA_RESIDUAL_TOL_BF16 = 0.75
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def bf16_dev(bits, dev="cuda"):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def f32_dev(a, dev="cuda"):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def words_host(words_t):
+    return words_t.cpu().numpy().view(np.uint32)
+
+
+def row_rel_l2(y, y_ref):
+    num = np.linalg.norm(y - y_ref, axis=1)
+    den = np.linalg.norm(y_ref, axis=1)
+    return num / np.maximum(den, 1e-300)
+
+
+def delta_residual(y, y_ref, y_delta):
+    """Per row ||y - y_ref|| / ||y_delta|| for rows whose delta term is nonzero."""
+    dn = np.linalg.norm(y_delta, axis=1)
+    keep = dn > 0
+    return np.linalg.norm(y - y_ref, axis=1)[keep] / dn[keep]
+
+
+def oracle_delta_term(x, variants, seg_offsets, seg_variant, d_out, d_in):
+    """alpha_v * x S_v^T per segment (the part of y the sign bits contribute), fp64."""
+    y = np.zeros((x.shape[0], d_out))
+    for s, v in enumerate(seg_variant):
+        lo, hi = seg_offsets[s], seg_offsets[s + 1]
+        if v < 0 or hi <= lo:
+            continue
+        words, alpha = variants[v]
+        sgn = O.unpack_signs_ref(words, d_in).astype(np.float64)
+        y[lo:hi] = np.float64(np.float32(alpha)) * (x[lo:hi] @ sgn.T)
+    return y
+
+
+def gpu_compress(deltas_np, dev="cuda"):
+    """Compress every delta on the device; returns [(words_t, alpha_t)]."""
+    import tenant_serving_bitdelta_amd as bd
+    torch = torch_mod()
+    out = []
+    for d in deltas_np:
+        dt = f32_dev(d, dev)
+        words = torch.empty((d.shape[0], d.shape[1] // 32), dtype=torch.int32, device=dev)
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+        bd.compress(dt, words, alpha)
+        out.append((words, alpha))
+    return out

@@ -1,0 +1,154 @@
+"""Host-side checks of libbitdelta that need no GPU: the library loads, exports every entry
+point include/bitdelta.h declares, plans segments like the oracle, and rejects every invalid
+argument on the host before anything is enqueued (fake device addresses are never touched on
+these paths)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.bitdelta_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitdelta.h")
+
+bd = pytest.importorskip("tenant_serving_bitdelta_amd")
+if not os.path.exists(bd.LIB_PATH):
+    pytest.skip("libbitdelta.so not built", allow_module_level=True)
+
+L = bd.lib()
+OK, INVALID, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+FAKE = 0x7F0000000000  # 256-byte aligned fake device address, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitdelta_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in bitdelta.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert bd.abi_version() == 1
+    for s in range(7):
+        assert L.bitdelta_status_string(s)
+    assert L.bitdelta_status_string(99) == b"unknown status"
+
+
+def test_sign_words_and_workspace():
+    assert bd.sign_words(4096, 4096) == 4096 * 128
+    assert bd.sign_words(256, 512) == 4096
+    assert bd.sign_words(8, 33) == -1 and bd.sign_words(-1, 32) == -1
+    # the packed matrix is 1/32 of fp32 storage: words * 4 bytes = d_out * d_in / 8
+    assert bd.sign_words(4096, 4096) * 4 == 4096 * 512
+    assert bd.compress_workspace_bytes(256, 512) >= 8
+    assert bd.compress_workspace_bytes(8192, 28672) % 8 == 0
+    assert bd.compress_workspace_bytes(8192, 28672) <= 2048 * 8
+    assert bd.compress_workspace_bytes(10, 31) == 0
+
+
+@pytest.mark.parametrize("m,nv,seed", [(0, 3, 0), (1, 1, 1), (7, 2, 2), (64, 14, 3), (256, 14, 4), (1000, 64, 5)])
+def test_plan_matches_oracle(m, nv, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, nv, size=m).astype(np.int32)
+    perm, offs, segv = bd.plan_segments(ids, nv)
+    rp, ro, rv = O.plan_segments_ref(ids, nv)
+    np.testing.assert_array_equal(perm, rp)
+    np.testing.assert_array_equal(offs, ro if m else np.array([0], np.int32))
+    np.testing.assert_array_equal(segv, rv)
+
+
+def test_plan_rejects_bad_ids():
+    with pytest.raises(bd.BitDeltaError) as e:
+        bd.plan_segments([0, 3], 3)
+    assert e.value.status == INVALID
+    with pytest.raises(bd.BitDeltaError):
+        bd.plan_segments([-2], 3)
+    with pytest.raises(bd.BitDeltaError):
+        bd.plan_segments([0], 65)
+
+
+def _compress(delta, d_out, d_in, words, alpha, ws, ws_bytes):
+    return L.bitdelta_compress(delta, d_out, d_in, words, alpha, ws, ws_bytes, None)
+
+
+def test_compress_validation():
+    ws = bd.compress_workspace_bytes(64, 64)
+    assert _compress(None, 64, 64, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress(FAKE, 64, 64, None, FAKE, FAKE, ws) == INVALID
+    assert _compress(FAKE, 0, 64, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress(FAKE, 64, 48, FAKE, FAKE, FAKE, ws) == SHAPE
+    assert _compress(FAKE + 4, 64, 64, FAKE, FAKE, FAKE, ws) == ALIGN
+    assert _compress(FAKE, 64, 64, FAKE + 2, FAKE, FAKE, ws) == ALIGN
+    assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE + 4, ws) == ALIGN
+    assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE, ws - 8) == WORKSPACE
+
+
+def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None):
+    o = np.ascontiguousarray(offs, dtype=np.int32)
+    v = np.ascontiguousarray(segv, dtype=np.int32)
+    op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    vp = v.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    varr = (bd._Variant * max(len(variants), 1))()
+    for i, (wd, al) in enumerate(variants):
+        varr[i].sign_words, varr[i].alpha = wd, al
+    if path is None:
+        return L.bitdelta_matmul(x, w, m, d_out, d_in, varr, len(variants), op, vp, v.size, y,
+                                 y_dtype, None)
+    prob = (bd._Problem * 1)()
+    prob[0].x, prob[0].w_base, prob[0].y = x, w, y
+    prob[0].d_out, prob[0].d_in = d_out, d_in
+    prob[0].variants = ctypes.cast(varr, ctypes.POINTER(bd._Variant))
+    prob[0].num_variants = len(variants)
+    return L.bitdelta_matmul_grouped(prob, 1, m, op, vp, v.size, y_dtype, path, None)
+
+
+def test_matmul_validation():
+    V = [(FAKE, FAKE), (FAKE + 256, FAKE + 512)]
+    good = dict(x=FAKE, w=FAKE, m=8, d_out=64, d_in=64, variants=V, offs=[0, 3, 8], segv=[0, 1], y=FAKE)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return _matmul(**a)
+
+    assert call(x=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(d_in=48) == SHAPE
+    assert call(d_out=0) == INVALID
+    assert call(offs=[0, 3, 7]) == SHAPE          # last offset != M
+    assert call(offs=[1, 3, 8]) == SHAPE          # first offset != 0
+    assert call(offs=[0, 5, 3, 8], segv=[0, 1, 0]) == SHAPE  # not monotone
+    assert call(segv=[0, 2]) == INVALID           # variant id out of range
+    assert call(segv=[-2, 1]) == INVALID
+    assert call(x=FAKE + 8) == ALIGN
+    assert call(w=FAKE + 2) == ALIGN
+    assert call(y=FAKE + 4) == ALIGN
+    assert call(variants=[(FAKE + 2, FAKE), (FAKE, FAKE)]) == ALIGN
+    assert call(variants=[(None, FAKE), (FAKE, FAKE)]) == INVALID
+    assert call(y_dtype=7) == INVALID
+    assert call(path=9) == INVALID
+    assert call(path=1) == UNSUPPORTED            # the GEMV path takes at most 4 tokens
+    # an unused variant may be absent
+    assert call(m=0, offs=[0, 0, 0]) == OK         # empty batch: nothing enqueued
+    assert call(m=0, offs=[0], segv=[]) == OK
+    assert call(m=0, offs=[0], segv=[], x=None, y=None) == OK  # empty tensors have no storage
+    assert call(m=0, offs=[0], segv=[], w=None) == INVALID
+
+
+def test_auto_path_choice():
+    assert bd.auto_path(1, [0, 1], [0]) == 1
+    assert bd.auto_path(4, [0, 2, 4], [0, 3]) == 1
+    assert bd.auto_path(64, [0, 64], [0]) == 2
+    assert bd.auto_path(256, [0, 100, 256], [-1, 5]) == 2
+    assert bd.auto_path(8192, [0, 2048, 4096, 6144, 8192], [0, 1, 2, 3]) == 3
+    assert bd.auto_path(8, [0, 9], [0]) == -1

@@ -1,0 +1,253 @@
+"""GPU parity at sizes the oracle finishes in seconds: every kernel path against the fp64 CPU
+oracle on the same seeded inputs, element by element, with shapes that span several tiles and
+a ragged tail, plus the degenerate cases of the method."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle.bitdelta_oracle as O
+import workloads as WL
+from parity import (DELTA_RESIDUAL_TOL_BF16, ROW_L2_TOL, bf16_dev, delta_residual, f32_dev,
+                    gpu_compress, oracle_delta_term, row_rel_l2, words_host)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+bd = pytest.importorskip("tenant_serving_bitdelta_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------------------------
+# compress
+# ----------------------------------------------------------------------------------------------
+
+def check_compress(delta):
+    (words, alpha), = gpu_compress([delta])
+    torch.cuda.synchronize()
+    ref_words, ref_alpha = O.compress_ref(delta)
+    np.testing.assert_array_equal(words_host(words), ref_words)
+    a = float(alpha.cpu()[0])
+    assert abs(a - float(ref_alpha)) <= 1e-6 * abs(float(ref_alpha)) or a == float(ref_alpha)
+    return words, alpha
+
+
+def test_compress_config1():
+    check_compress(WL.config1()["deltas"][0])
+
+
+@pytest.mark.parametrize("d_out,d_in,seed", [(1, 32, 1), (3, 64, 2), (17, 96, 3), (64, 1056, 4),
+                                             (255, 512, 5), (1000, 4096, 6), (33, 8192, 7)])
+def test_compress_shapes(d_out, d_in, seed):
+    rng = np.random.default_rng(seed)
+    d = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
+    d[rng.random(d.shape) < 0.02] = 0.0
+    check_compress(d)
+
+
+def test_compress_special_values():
+    d = np.zeros((4, 64), dtype=np.float32)
+    d[0, :8] = [-0.0, 0.0, -1e-45, 1e-45, -1e-40, 1e-40, -1.17e-38, 3.0]
+    d[1] = -1.0
+    d[2] = 2.0
+    d[3, ::3] = -5e-4
+    words, alpha = check_compress(d)
+    w = words_host(words)
+    assert w[1, 0] == 0 and w[1, 1] == 0 and w[2, 0] == 0xFFFFFFFF
+    assert w[0, 0] & 0xFF == 0b10101011  # +0,-0 -> 1; negative subnormals -> 0; positives -> 1
+
+
+def test_compress_all_zero_and_repeatable():
+    d = np.zeros((16, 256), dtype=np.float32)
+    words, alpha = check_compress(d)
+    assert float(alpha.cpu()[0]) == 0.0 and np.all(words_host(words) == 0xFFFFFFFF)
+    rng = np.random.default_rng(11)
+    d = rng.laplace(0, 2e-4, size=(300, 2048)).astype(np.float32)
+    (w1, a1), (w2, a2) = gpu_compress([d, d])
+    torch.cuda.synchronize()
+    assert torch.equal(w1, w2) and torch.equal(a1, a2)
+
+
+# ----------------------------------------------------------------------------------------------
+# fused matmul
+# ----------------------------------------------------------------------------------------------
+
+def run_matmul(case, path, out_dtype, check_delta=True):
+    w_bits, x_bits = case["w"], case["x"]
+    d_out, d_in = w_bits.shape
+    nv = len(case["deltas"])
+    ids = case["token_variant"]
+    perm, offs, segv = bd.plan_segments(ids, nv)
+    var_gpu = gpu_compress(case["deltas"])
+    var_ref = [O.compress_ref(d) for d in case["deltas"]]
+    w = bf16_dev(w_bits)
+    x = bf16_dev(x_bits[perm])
+    y = bd.matmul(x, w, var_gpu, offs, segv, out_dtype=out_dtype, path=path)
+    torch.cuda.synchronize()
+    xf = O.bf16_bits_to_f64(x_bits)[perm]
+    wf = O.bf16_bits_to_f64(w_bits)
+    y_ref = O.matmul_ref(xf, wf, var_ref, offs, segv)
+    y_got = y.float().cpu().numpy().astype(np.float64)
+    rel = row_rel_l2(y_got, y_ref)
+    assert rel.max() <= ROW_L2_TOL, f"row rel L2 {rel.max():.3e}"
+    y_delta = oracle_delta_term(xf, var_ref, offs, segv, d_out, d_in)
+    dres = delta_residual(y_got, y_ref, y_delta)
+    if out_dtype == "f32":
+        # fp32 output: decode paths keep W_eff exact (fp32 accumulation only)
+        lim = (5e-3, 0.75) if path == "prefill" else (1e-5, 1e-2)
+        assert rel.max() <= lim[0], f"f32 row rel L2 {rel.max():.3e}"
+        if check_delta and dres.size:
+            assert dres.max() <= lim[1], f"delta residual {dres.max():.3e}"
+    elif check_delta and dres.size:
+        assert dres.max() <= DELTA_RESIDUAL_TOL_BF16, f"delta residual {dres.max():.3e}"
+    return y, y_ref, perm, offs, segv
+
+
+PATH_CASES = [
+    # (name, d_out, d_in, M, variants, base_frac, paths)
+    ("tiny", 16, 32, 1, 1, 0.0, ("gemv", "stream", "prefill")),
+    ("m3-ragged", 70, 96, 3, 2, 0.3, ("gemv", "stream", "prefill")),
+    ("m4-mixed", 200, 1056, 4, 3, 0.25, ("gemv", "stream", "prefill")),
+    ("m17", 130, 544, 17, 5, 0.1, ("stream", "prefill")),
+    ("m64-14v", 192, 1024, 64, 14, 0.0, ("stream", "prefill")),
+    ("m130", 96, 2080, 130, 6, 0.2, ("stream", "prefill")),
+    ("m256-zipf", 128, 512, 256, 14, 0.0, ("stream", "prefill")),
+    ("m300-chunks", 64, 256, 300, 14, 0.05, ("stream", "prefill")),
+    ("m600", 136, 320, 600, 3, 0.1, ("prefill", "stream")),
+]
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: c[0])
+def test_matmul_paths(case, out_dtype):
+    name, d_out, d_in, m, nv, base_frac, paths = case
+    dist = "zipf" if "zipf" in name else "uniform"
+    c = WL.linear_case(seed=zlib.crc32(name.encode()) % 1000, d_out=d_out, d_in=d_in, m=m, num_variants=nv,
+                       dist=dist, base_frac=base_frac, zero_frac=0.01)
+    for path in paths:
+        print(f"  path={path}", flush=True)
+        run_matmul(c, path, out_dtype)
+
+
+def test_config1_all_paths():
+    c = WL.config1()
+    for path in ("auto", "gemv", "stream", "prefill"):
+        for out in ("bf16", "f32"):
+            run_matmul(c, path, out)
+
+
+def test_identity_readback_exact():
+    """x = I reads every reconstructed weight back through the product: with fp32 output the
+    decode paths give fp32(w + alpha*s) exactly (one rounding), prefill bf16 of that value."""
+    rng = np.random.default_rng(21)
+    d_out, d_in = 80, 64
+    w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
+    delta = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
+    x_bits = WL.f32_to_bf16_bits(np.eye(d_in, dtype=np.float32))
+    (words, alpha), = gpu_compress([delta])
+    ref_words, ref_alpha = O.compress_ref(delta)
+    weff = O.reconstruct_ref(O.bf16_bits_to_f64(w_bits), ref_words, ref_alpha)  # fp64 exact
+    want_f32 = weff.astype(np.float32).T
+    want_bf16 = O.bf16_bits_to_f64(WL.f32_to_bf16_bits(weff.astype(np.float32))).T
+    for path in ("stream", "prefill"):
+        y = bd.matmul(bf16_dev(x_bits), bf16_dev(w_bits), [(words, alpha)], [0, d_in], [0],
+                      out_dtype="f32", path=path)
+        got = y.cpu().numpy()
+        want = want_bf16 if path == "prefill" else want_f32
+        np.testing.assert_array_equal(got, want.astype(np.float32), err_msg=path)
+
+
+def test_gemv_readback_exact():
+    rng = np.random.default_rng(22)
+    d_out, d_in = 40, 96
+    w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
+    delta = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
+    (words, alpha), = gpu_compress([delta])
+    ref_words, ref_alpha = O.compress_ref(delta)
+    weff = O.reconstruct_ref(O.bf16_bits_to_f64(w_bits), ref_words, ref_alpha).astype(np.float32)
+    for k in (0, 31, 32, 95):
+        x = np.zeros((1, d_in), np.float32)
+        x[0, k] = 1.0
+        y = bd.matmul(bf16_dev(WL.f32_to_bf16_bits(x)), bf16_dev(w_bits), [(words, alpha)],
+                      [0, 1], [0], out_dtype="f32", path="gemv")
+        np.testing.assert_array_equal(y.cpu().numpy()[0], weff[:, k])
+
+
+def test_zero_base_isolates_delta():
+    """W_base = 0: y = alpha * x S^T, so sign or alpha mistakes show at full size."""
+    rng = np.random.default_rng(23)
+    d_out, d_in, m = 96, 512, 20
+    c = {"w": np.zeros((d_out, d_in), np.uint16),
+         "deltas": [rng.laplace(0, 4e-4, size=(d_out, d_in)).astype(np.float32) for _ in range(2)],
+         "x": WL.f32_to_bf16_bits(rng.normal(size=(m, d_in)).astype(np.float32)),
+         "token_variant": rng.integers(0, 2, size=m).astype(np.int32)}
+    for path in ("stream", "prefill"):
+        run_matmul(c, path, "f32")
+    c["x"], c["token_variant"] = c["x"][:3], c["token_variant"][:3]
+    run_matmul(c, "gemv", "f32")
+
+
+def test_zero_delta_and_base_only_tokens():
+    rng = np.random.default_rng(24)
+    d_out, d_in, m = 72, 256, 40
+    c = {"w": WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32)),
+         "deltas": [np.zeros((d_out, d_in), np.float32)],
+         "x": WL.f32_to_bf16_bits(rng.normal(size=(m, d_in)).astype(np.float32)),
+         "token_variant": np.where(np.arange(m) % 3 == 0, -1, 0).astype(np.int32)}
+    for path in ("stream", "prefill"):
+        y, y_ref, *_ = run_matmul(c, path, "f32", check_delta=False)
+
+
+def test_empty_batch_is_noop():
+    w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((0, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    bd.matmul(x, w, [], [0], [], y=y)
+
+
+def test_batch_invariance_and_repeatability():
+    """A token's output does not depend on the rest of the batch, and reruns are bit-identical."""
+    c = WL.linear_case(seed=31, d_out=160, d_in=768, m=90, num_variants=5, base_frac=0.1)
+    perm, offs, segv = bd.plan_segments(c["token_variant"], 5)
+    var_gpu = gpu_compress(c["deltas"])
+    w = bf16_dev(c["w"])
+    x = bf16_dev(c["x"][perm])
+    for path in ("stream", "prefill"):
+        y1 = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path=path)
+        y2 = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path=path)
+        assert torch.equal(y1, y2)
+        for s in range(len(segv)):
+            lo, hi = int(offs[s]), int(offs[s + 1])
+            ys = bd.matmul(x[lo:hi].contiguous(), w, var_gpu, [0, hi - lo], [segv[s]],
+                           out_dtype="f32", path=path)
+            assert torch.equal(ys, y1[lo:hi]), (path, s)
+
+
+def test_grouped_matches_single():
+    c1 = WL.linear_case(seed=41, d_out=200, d_in=512, m=48, num_variants=4)
+    rng = np.random.default_rng(42)
+    w2 = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(72, 1024)).astype(np.float32))
+    x2 = WL.f32_to_bf16_bits(rng.normal(size=(48, 1024)).astype(np.float32))
+    d2 = [rng.laplace(0, 2e-4, size=(72, 1024)).astype(np.float32) for _ in range(4)]
+    perm, offs, segv = bd.plan_segments(c1["token_variant"], 4)
+    v1, v2 = gpu_compress(c1["deltas"]), gpu_compress(d2)
+    xa, wa = bf16_dev(c1["x"][perm]), bf16_dev(c1["w"])
+    xb, wb = bf16_dev(x2[perm]), bf16_dev(w2)
+    ya = torch.empty((48, 200), dtype=torch.float32, device="cuda")
+    yb = torch.empty((48, 72), dtype=torch.float32, device="cuda")
+    bd.matmul_grouped([(xa, wa, ya, v1), (xb, wb, yb, v2)], offs, segv, out_dtype="f32",
+                      path="stream")
+    sa = bd.matmul(xa, wa, v1, offs, segv, out_dtype="f32", path="stream")
+    sb = bd.matmul(xb, wb, v2, offs, segv, out_dtype="f32", path="stream")
+    assert torch.equal(ya, sa) and torch.equal(yb, sb)
+    ref_b = O.matmul_ref(O.bf16_bits_to_f64(x2)[perm], O.bf16_bits_to_f64(w2),
+                         [O.compress_ref(d) for d in d2], offs, segv)
+    assert row_rel_l2(yb.cpu().numpy().astype(np.float64), ref_b).max() <= 1e-5
