@@ -1,0 +1,324 @@
+"""Benchmark of the BitDelta hot path on one MI355X.
+
+Default workload (headline): a stack of 20 decoder blocks of a 70B-class model (q, o 8192x8192;
+k, v 1024x8192; gate, up 28672x8192; down 8192x28672), 14 fine-tuned variants resident as
+1-bit deltas.  Set-up compresses all 14 x 140 deltas on the GPU (alpha + sign packing,
+Laplace(0, b) deltas drawn per matrix and discarded), then a step is one decode pass of a
+256-token batch whose variant ids follow a truncated Zipf(1.1) over the 14 variants: the
+segment plan plus one grouped fused reconstruct-and-multiply launch per block over its seven
+linears (independent synthetic activations per linear).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+Other workloads (--config): 2 = one down_proj GEMV (1 token, 1 variant), 3 = one block with a
+64-token uniform batch, 4 = prefill of gate and up with 4 requests x 2048 tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as WL  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+NUM_VARIANTS = 14
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=5, choices=(2, 3, 4, 5))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------------------------
+# workload construction (device memory via torch; all compute in libbitdelta)
+# ---------------------------------------------------------------------------------------------
+
+class Linear:
+    def __init__(self, name, d_out, d_in):
+        self.name, self.d_out, self.d_in = name, d_out, d_in
+        self.w = None
+        self.variants = []
+        self.x = None
+        self.y = None
+
+
+def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nvar=NUM_VARIANTS):
+    dev = "cuda"
+    maxn = max(d_out * d_in for _, d_out, d_in in linears)
+    dbuf = torch.empty(maxn, dtype=torch.float32, device=dev)
+    ws = torch.empty(2048, dtype=torch.float64, device=dev)
+    layers = []
+    for b in range(blocks):
+        blk = []
+        for name, d_out, d_in in linears:
+            L = Linear(name, d_out, d_in)
+            L.w = WL.gpu_normal_bf16(torch, (d_out, d_in), 0.02, WL.substream_seed(config, b, name, "w"))
+            for v in range(nvar):
+                delta = WL.gpu_laplace_f32(torch, (d_out, d_in), scales[v],
+                                           WL.substream_seed(config, b, name, v, "delta"),
+                                           out=dbuf[:d_out * d_in])
+                words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device=dev)
+                alpha = torch.empty(1, dtype=torch.float32, device=dev)
+                compress_timer.start()
+                bd.compress(delta, words, alpha, workspace=ws)
+                compress_timer.stop(4 * d_out * d_in + d_out * d_in // 8 + 4)
+                L.variants.append((words, alpha))
+            blk.append(L)
+        layers.append(blk)
+        log(f"[setup] block {b + 1}/{blocks} built and compressed")
+    del dbuf
+    return layers
+
+
+class EventTimer:
+    """Sums kernel durations between pairs of HIP events on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+        self.bytes = 0
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self._open = e
+
+    def stop(self, nbytes=0):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((self._open, e))
+        self.bytes += nbytes
+
+    def total_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+
+def decode_bytes(blk, m, n_active):
+    tot = 0
+    for L in blk:
+        n = L.d_out * L.d_in
+        tot += 2 * n + n_active * (n // 8 + 4) + 2 * m * L.d_in + 2 * m * L.d_out
+    return tot
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the same workload
+# ---------------------------------------------------------------------------------------------
+
+def cpu_baseline_decode(torch, config, linears_sample, scales, perm, offs, segv, m, total_elems, nvar):
+    from oracle import bitdelta_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    elapsed, elems = 0.0, 0
+    for name, d_out, d_in in linears_sample:
+        # regenerate the sampled linear's inputs from the same seeds (device draw, host copy)
+        w = WL.gpu_normal_bf16(torch, (d_out, d_in), 0.02, WL.substream_seed(config, 0, name, "w"))
+        wf = w.float().cpu().numpy().astype(np.float64)
+        variants = []
+        for v in range(nvar):
+            d = WL.gpu_laplace_f32(torch, (d_out, d_in), scales[v],
+                                   WL.substream_seed(config, 0, name, v, "delta")).cpu().numpy()
+            variants.append(O.compress_ref(d))
+        x = WL.gpu_normal_bf16(torch, (m, d_in), 1.0, WL.substream_seed(config, 0, name, "x"))
+        xf = x.float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        O.matmul_ref(xf, wf, variants, offs, segv)
+        elapsed += time.perf_counter() - t0
+        elems += d_out * d_in
+        log(f"[cpu baseline] oracle on {name} ({d_out}x{d_in}): {elapsed:.1f}s so far")
+    est_step = elapsed * total_elems / elems
+    return {"value": m / est_step, "unit": "tokens/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"oracle matmul of block 0's {'+'.join(n for n, _, _ in linears_sample)} "
+                       f"({elems} weights, all {m} tokens, {nvar} variant(s)) in {elapsed:.1f}s on the host, "
+                       f"scaled by weight count to the full step ({total_elems} weights); "
+                       f"numpy elementwise on 1 thread, BLAS on {blas_threads}")}
+
+
+# ---------------------------------------------------------------------------------------------
+
+def run_decode(args, torch, bd, config):
+    if config == 5:
+        blocks, m, dist = 20, 256, "zipf"
+        linears = list(WL.BLOCK_LINEARS)
+    elif config == 3:
+        blocks, m, dist = 1, 64, "uniform"
+        linears = list(WL.BLOCK_LINEARS)
+    else:  # config 2
+        blocks, m, dist = 1, 1, "uniform"
+        linears = [("down", 8192, 28672)]
+    scales = WL.decode_variant_scales(config) if config != 2 else np.array([2e-4])
+    nvar = NUM_VARIANTS if config != 2 else 1
+    ids = WL.decode_token_ids(config, m, nvar, dist)
+    perm, offs, segv = bd.plan_segments(ids, nvar)
+    n_active = int(np.sum(segv >= 0))
+    log(f"[setup] config {config}: {blocks} block(s), M={m}, segments={list(np.diff(offs))}")
+
+    comp = EventTimer(torch)
+    layers = build_layers(torch, bd, config, blocks, linears, scales, comp, nvar)
+    comp_ms = comp.total_ms()
+    for b, blk in enumerate(layers):
+        for L in blk:
+            L.x = WL.gpu_normal_bf16(torch, (m, L.d_in), 1.0, WL.substream_seed(config, b, L.name, "x"))
+            L.y = torch.empty((m, L.d_out), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(timer=None):
+        # plan (host) + one grouped launch per block
+        _, o, s = bd.plan_segments(ids, nvar)
+        for blk in layers:
+            probs = [(L.x, L.w, L.y, L.variants) for L in blk]
+            if timer:
+                timer.start()
+            bd.matmul_grouped(probs, o, s)
+            if timer:
+                timer.stop()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kt = EventTimer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(kt)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = kt.total_ms()
+    launches = len(kt.pairs)
+    bytes_launch = decode_bytes(layers[0], m, n_active)  # every block has the same shapes
+    avg_launch_s = kern_ms / launches / 1e3
+    achieved = bytes_launch / avg_launch_s / 1e9
+    total_elems = sum(L.d_out * L.d_in for blk in layers for L in blk)
+    path = bd.auto_path(m, offs, segv)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample = [l for l in linears if l[0] in ("k", "v", "q")] or linears
+        cpu = cpu_baseline_decode(torch, config, sample, scales, perm, offs, segv, m, total_elems,
+                                  nvar)
+
+    comp_bytes = comp.bytes
+    names = {2: "down_proj GEMV 8192x28672, 1 token, 1 variant",
+             3: "one 70B decoder block (7 linears), 64-token uniform batch, 14 variants",
+             5: "20 x 70B decoder blocks (140 linears), 256-token Zipf(1.1) batch, 14 variants"}
+    return {
+        "metric": "fused BitDelta matmul tokens/s + achieved HBM GB/s (% peak), 14 variants",
+        "value": m * 1e3 / ms_step,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulate)", "data": "synthetic (seeded; random weights/deltas)",
+        "config": {"workload": names[config], "config_index": config, "tokens_per_step": m,
+                   "segments": [int(v) for v in np.diff(offs)], "active_variants": n_active,
+                   "launches_per_step": launches // args.steps,
+                   "kernel_path": {1: "gemv", 2: "stream", 3: "prefill"}[path],
+                   "parallelism": "single GPU"},
+        "hbm_gbs_step": bytes_launch * len(layers) / (ms_step / 1e3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "stream_kernel" if path == 2 else "gemv_kernel",
+                     "bytes_per_launch": bytes_launch, "avg_launch_us": avg_launch_s * 1e6},
+        "compress": {"matrices": len(comp.pairs), "bytes": comp_bytes, "ms": comp_ms,
+                     "gbs": comp_bytes / (comp_ms / 1e3) / 1e9,
+                     "frac": comp_bytes / (comp_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_prefill(args, torch, bd):
+    config = 4
+    linears = [("gate", 28672, 8192), ("up", 28672, 8192)]
+    scales = WL.decode_variant_scales(config)
+    req_var = WL.prefill_request_variants(config, 4, NUM_VARIANTS)
+    ids = np.repeat(req_var, 2048).astype(np.int32)
+    perm, offs, segv = bd.plan_segments(ids, NUM_VARIANTS)
+    m = ids.size
+    comp = EventTimer(torch)
+    layers = build_layers(torch, bd, config, 1, linears, scales, comp)[0]
+    for L in layers:
+        L.x = WL.gpu_normal_bf16(torch, (m, L.d_in), 1.0, WL.substream_seed(config, 0, L.name, "x"))
+        L.y = torch.empty((m, L.d_out), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(timer=None):
+        _, o, s = bd.plan_segments(ids, NUM_VARIANTS)
+        probs = [(L.x, L.w, L.y, L.variants) for L in layers]
+        if timer:
+            timer.start()
+        bd.matmul_grouped(probs, o, s, path="prefill")
+        if timer:
+            timer.stop()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kt = EventTimer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(kt)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = kt.total_ms() / len(kt.pairs)
+    flops = sum(2.0 * m * L.d_out * L.d_in for L in layers)
+    achieved = flops / (kern_ms / 1e3) / 1e12
+    return {
+        "metric": "fused BitDelta matmul tokens/s (prefill, bf16 MFMA), 14 variants resident",
+        "value": m * 1e3 / ms_step, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded; random weights/deltas)",
+        "config": {"workload": "prefill gate+up 28672x8192, 4 requests x 2048 tokens on 4 of 14 variants",
+                   "config_index": 4, "tokens_per_step": m, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_kernel", "flops_per_launch": flops,
+                     "avg_launch_us": kern_ms * 1e3},
+        "cpu_baseline": None,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the BitDelta hot "
+              "path here is single-GPU and multi-GPU runs are not part of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tenant_serving_bitdelta_amd as bd
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.config == 4:
+        res = run_prefill(args, torch, bd)
+    else:
+        res = run_decode(args, torch, bd, args.config)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,6 +66,16 @@ int pick_path(int64_t M) {
   return BITDELTA_PATH_PREFILL;
 }
 
+// The streaming kernel reads sign words 16 bytes (4 K steps) per row at a time.
+bool stream_eligible(const bitdelta_problem* probs, int np, const std::vector<Segment>& segs) {
+  for (int p = 0; p < np; ++p) {
+    if (probs[p].d_in % 128 != 0) return false;
+    for (const Segment& s : segs)
+      if (s.variant >= 0 && !aligned(probs[p].variants[s.variant].sign_words, 16)) return false;
+  }
+  return true;
+}
+
 // ---- GEMV: one launch per linear ----------------------------------------------------------
 bitdelta_status run_gemv(const bitdelta_problem* probs, int np, int64_t M,
                          const std::vector<Segment>& segs, int y_f32, hipStream_t st) {
@@ -118,7 +128,7 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
     const int base_row = tiles[t0].row;
     while (t1 < tiles.size() && (int)(t1 - t0) < bd::kStreamMaxTiles) {
       const Tile& t = tiles[t1];
-      if (t.row + t.valid - base_row > bd::kStreamMaxM) break;
+      if (t.row + t.valid - base_row > 32767) break;  // tile offsets are 16-bit
       if (t.variant >= 0) {
         bool have = !slot_var.empty() && slot_var.back() == t.variant;
         if (!have && (int)slot_var.size() == bd::kMaxSlots) break;
@@ -130,14 +140,16 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
     bd::StreamArgs a;
     memset(&a, 0, sizeof(a));
     a.ntiles = (int)(t1 - t0);
-    a.nslots = (int)slot_var.size();
+    // base-only batches still get one (dummy) slot: the kernel reads it and scales it by 0
+    a.nslots = slot_var.empty() ? 1 : (int)slot_var.size();
     a.M = rows;
     a.y_f32 = y_f32;
     for (size_t i = t0; i < t1; ++i) {
       const Tile& t = tiles[i];
       int slot = -1;
-      for (int q = 0; q < a.nslots; ++q)
-        if (slot_var[q] == t.variant) slot = q;
+      if (t.variant >= 0)
+        for (int q = 0; q < (int)slot_var.size(); ++q)
+          if (slot_var[q] == t.variant) slot = q;
       a.tile_slot[i - t0] = (int8_t)slot;
       a.tile_valid[i - t0] = (uint8_t)t.valid;
       a.tile_src[i - t0] = (int16_t)(t.row - base_row);
@@ -156,9 +168,14 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
         S.d_out = (int)P.d_out;
         S.d_in = (int)P.d_in;
         S.block_begin = blocks;
-        for (int s = 0; s < a.nslots; ++s) {
+        for (int s = 0; s < (int)slot_var.size(); ++s) {
           S.words[s] = P.variants[slot_var[s]].sign_words;
           S.alpha[s] = P.variants[slot_var[s]].alpha;
+        }
+        if (slot_var.empty()) {
+          // W_base is at least 16x larger than a sign-word matrix of the same shape
+          S.words[0] = static_cast<const uint32_t*>(P.w_base);
+          S.alpha[0] = nullptr;
         }
         blocks += (int)((P.d_out + bd::kStreamRowsPerBlock - 1) / bd::kStreamRowsPerBlock);
       }
@@ -324,8 +341,13 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
     if (s != BITDELTA_OK) return s;
   }
   if (M == 0) return BITDELTA_OK;
+  const bool explicit_path = path != BITDELTA_PATH_AUTO;
   if (path == BITDELTA_PATH_AUTO) path = pick_path(M);
   if (path == BITDELTA_PATH_GEMV && M > 4) return BITDELTA_ERR_UNSUPPORTED;
+  if (path == BITDELTA_PATH_STREAM && !stream_eligible(problems, num_problems, segs)) {
+    if (explicit_path) return BITDELTA_ERR_UNSUPPORTED;
+    path = BITDELTA_PATH_PREFILL;
+  }
   const int y_f32 = y_dtype == BITDELTA_OUT_F32;
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (path) {

@@ -51,9 +51,10 @@ struct GemvArgs {
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
-// Streaming decode: token tiles of 16 rows, each tile within one segment.
+// Streaming decode: token tiles of 16 rows, each tile within one segment.  Needs d_in % 128 == 0
+// and 16-byte aligned sign words; at least one slot (a readable dummy when no variant is used).
 constexpr int kStreamMaxTiles = 24;
-constexpr int kStreamMaxM = 256;
+constexpr int kStreamMaxM = 256;   // batches up to this size go to the streaming path by default
 constexpr int kStreamRowsPerBlock = 64;
 
 struct StreamProblem {
@@ -75,6 +76,7 @@ struct StreamArgs {
   int16_t tile_src[kStreamMaxTiles];   // first x row of the tile
 };
 hipError_t launch_stream(const StreamArgs& a, int nblocks, hipStream_t stream);
+size_t stream_lds_bytes(int ntiles, int nslots);
 
 // Prefill: per-segment tiles of 256 tokens x 128 output rows, W_eff rebuilt in LDS.
 constexpr int kPrefillBM = 256;

@@ -8,33 +8,41 @@
 // the sign part are both exact bf16 x bf16 products accumulated in fp32 by MFMA, and alpha_v is
 // applied once in fp32 at the end.  W_eff is never formed in memory.
 //
-// Work split.  A workgroup (4 waves) owns 64 output rows of one linear; wave w owns rows
-// 16w..16w+15 and keeps, for every 16-token tile of the batch, two 16x16 fp32 accumulators
-// (base and sign).  Tiles never straddle a segment, so each tile has one variant.  The K loop
-// walks d_in in steps of 64:
-//   * the batch's activations for the step are staged in LDS (one copy, read by all 4 waves);
-//   * the variants' sign words for the workgroup's rows are staged in LDS;
-//   * each wave loads its 16x64 bf16 block of W_base straight into registers (16-byte loads,
-//     prefetched one step ahead) as the A operand of v_mfma_f32_16x16x32_bf16;
-//   * per 32-wide chunk and variant, the 32-bit sign word of each row is expanded in registers
-//     into a bf16 +-1 A operand: a byte permute puts the lane's 8 bits in both 16-bit halves,
-//     a packed 16-bit shift moves bit pair (2d, 2d+1) to the two bf16 sign positions, and one
-//     3-input bit operation merges them with the constant 1.0 (2 VALU ops per 2 weights);
-//   * for every tile: B = the tile's activations (16 tokens x 32 k from LDS), then
-//     acc_base += W * B and, for a variant tile, acc_sign += S_v * B.
+// Work split.  A workgroup (8 waves, two per SIMD) owns 64 output rows of one linear; the
+// batch is cut into 16-token tiles that never straddle a segment (one variant per tile), and
+// wave w owns tiles [w*NTW, w*NTW+NTW).  For each of its tiles and each of the 4 row tiles it
+// keeps two 16x16 fp32 accumulators (base and sign).  The K loop walks d_in in steps of 64 (two
+// 32-wide chunks of v_mfma_f32_16x16x32_bf16):
+//   * a wave loads its own tiles' activations straight from global memory into B-operand
+//     registers (16 bytes per lane, one step ahead): activations are never staged in LDS, and no
+//     wave reads another wave's tokens;
+//   * the 64x64 block of W_base and the sign words of every active variant for the 64 rows
+//     (16 bytes = 4 steps per row and variant at a time) are loaded two steps ahead into
+//     registers and committed to double-buffered LDS, where all 8 waves read them; one
+//     workgroup barrier per step, which does not wait for outstanding global loads;
+//   * per chunk, tile and row tile the variant's 32-bit sign word of each row is expanded in
+//     registers into a bf16 +-1 A operand: a byte permute puts the lane's 8 bits in both 16-bit
+//     halves, a packed 16-bit shift moves bit pair (2d, 2d+1) to the two bf16 sign positions,
+//     and one 3-input bit operation merges them with the constant 1.0 (2 VALU ops per 2
+//     weights); consecutive tiles of the same variant reuse the expansion;
+//   * acc_base += W * X_tile and acc_sign += S_v * X_tile.
 // Epilogue: y = acc_base + alpha_v * acc_sign, rounded to bf16 (nearest-even) or stored fp32.
+#include <type_traits>
+
 #include "bd_internal.h"
 
 namespace bd {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kKS = 64;            // k per step
-constexpr int kXStride = kKS + 8;  // bf16 per staged activation row (16 bytes of padding)
-constexpr int kXPieces = kStreamMaxM * (kKS / 8) / kThreads;  // 16-byte pieces per thread
-constexpr int kBitPieces = kMaxSlots * kStreamRowsPerBlock / kThreads;  // 8-byte pieces
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kKS = 64;                     // k per step
+constexpr int kRows = kStreamRowsPerBlock;  // 64 output rows per workgroup
+constexpr int kRT = kRows / 16;             // row tiles
+constexpr int kRowBytes = kKS * 2;          // bytes of one staged 64-wide bf16 row
+constexpr int kBitsRowBytes = 32;           // 8 sign words (4 steps) per row and variant
+constexpr unsigned kWBytes = kRows * kRowBytes;
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -56,212 +64,256 @@ __device__ __forceinline__ u32x4 expand_signs(unsigned word, unsigned byte_sel) 
   return r;
 }
 
-template <int NT>
+// Workgroup barrier ordering LDS traffic only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <typename T>
+__device__ __forceinline__ T* lds_at(unsigned char* base, unsigned off) {
+  return reinterpret_cast<T*>(base + off);
+}
+
+// NTW: token tiles per wave (the batch has at most 8*NTW tiles).
+template <int NTW>
 __global__ __launch_bounds__(kThreads, 1) void stream_kernel(const StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  // ---- which linear and which 64-row block -------------------------------------------------
+  // ---- which linear and which 64-row block (all wave-uniform) --------------------------------
   const int bid = blockIdx.x;
   int p = 0;
-  for (int q = 1; q < a.nprob; ++q)
-    if (bid >= a.prob[q].block_begin) p = q;
-  const StreamProblem& P = a.prob[p];
-  const int d_in = P.d_in, d_out = P.d_out, M = a.M;
-  const int row0 = (bid - P.block_begin) * kStreamRowsPerBlock;
-  const int T = a.ntiles, NS = a.nslots;
+#pragma unroll
+  for (int q = 1; q < kMaxProblems; ++q)
+    if (q < a.nprob && bid >= a.prob[q].block_begin) p = q;
+  const uint16_t* __restrict__ xg = a.prob[p].x;
+  const uint16_t* __restrict__ wg = a.prob[p].w;
+  const int d_in = a.prob[p].d_in, d_out = a.prob[p].d_out;
+  const int row0 = (bid - a.prob[p].block_begin) * kRows;
+  const int T = a.ntiles;   // 1..8*NTW
+  const int NS = a.nslots;  // >= 1 (the host supplies a readable dummy when no variant is used)
   const int wpr = d_in >> 5;
-  const int nsteps = (d_in + kKS - 1) / kKS;
+  const int nsteps = d_in / kKS;  // even: d_in is a multiple of 128 on this path
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
   const unsigned byte_sel = (unsigned)g | 0x0C00u | ((unsigned)g << 16) | 0x0C000000u;
 
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                         // [2][M][kXStride]
-  uint32_t* bs = reinterpret_cast<uint32_t*>(smem + 2 * M * kXStride * 2);  // [2][NS][64][2]
+  const unsigned bs_bytes = (unsigned)NS * kRows * kBitsRowBytes;
+  unsigned char* WS = smem;                 // [2][64 rows][128 B], 16-byte columns swizzled
+  unsigned char* BS = smem + 2 * kWBytes;   // [2][NS][64 rows][32 B]
 
-  // ---- per-lane W_base row (A operand rows) and staged-activation row per tile --------------
-  const int wrow = min(row0 + wave * 16 + j, d_out - 1);
-  const uint16_t* wp = P.w + (size_t)wrow * d_in + 8 * g;
-  int xoff[NT];  // bf16 offset of this lane's B-operand row inside one staging buffer
+  // ---- this wave's tiles ------------------------------------------------------------------------
+  int xoff[NTW];           // element offset of this lane's activation row (+ its 8-wide k group)
+  unsigned tslot[NTW];     // byte offset of the tile's variant inside a sign-word buffer
+  bool treal[NTW];         // tile exists (wave-uniform)
+  bool tnew[NTW];          // tile's variant differs from the previous tile's (wave-uniform)
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int r = i < T ? min((int)a.tile_src[i] + j, M - 1) : 0;
-    xoff[i] = r * kXStride + 8 * g;
+  for (int i = 0; i < NTW; ++i) {
+    const int ti_raw = wave * NTW + i;
+    const int ti = min(ti_raw, T - 1);
+    const int valid = a.tile_valid[ti];
+    xoff[i] = (a.tile_src[ti] + min(j, valid - 1)) * d_in + 8 * g;
+    const int s = a.tile_slot[ti];
+    tslot[i] = __builtin_amdgcn_readfirstlane((unsigned)((s < 0 ? 0 : s) * kRows * kBitsRowBytes));
+    treal[i] = ti_raw < T;
+    tnew[i] = i == 0 || a.tile_slot[min(ti_raw - 1, T - 1)] != s;
   }
 
-  // ---- staging helpers ----------------------------------------------------------------------
-  // activations: M rows x 64 k, 8 pieces of 16 bytes per row
-  u32x4 xr[kXPieces];
-  auto load_x = [&](int ks) {
+  // ---- staging of W_base and sign words (all threads) ---------------------------------------
+  const int wr_row = tid >> 3, wr_col = tid & 7;  // one 16-byte piece per thread per step
+  const int wsrc = min(row0 + wr_row, d_out - 1) * d_in + (wr_col ^ (wr_row & 7)) * 8;
+  const unsigned wdst = (unsigned)(wr_row * kRowBytes + wr_col * 16);
+  // sign words: per 4-step group NS x 64 rows x 2 pieces of 16 B; at each step a thread moves
+  // piece id = tid + 512 * (step % 4): slot id / 128 (wave-uniform), row (id / 2) % 64,
+  // half id % 2.  Rows 8..15 of every 16 swap halves (bank spread on reads).
+  const int brow = (tid >> 1) & 63, bhalf = tid & 1;
+  const int bgrow = min(row0 + brow, d_out - 1);
+  const unsigned bdst = (unsigned)(brow * kBitsRowBytes + ((bhalf ^ ((brow >> 3) & 1)) * 16));
+  const int bslot_base = wave >> 1;
+
+  // ---- per-lane LDS read offsets ----------------------------------------------------------------
+  unsigned aoff[2];  // + rt * 16 * kRowBytes
 #pragma unroll
-    for (int q = 0; q < kXPieces; ++q) {
-      const int pc = tid + q * kThreads;
-      const int r = pc >> 3, c = pc & 7;
-      const int k = ks * kKS + c * 8;
-      if (r < M && k < d_in)
-        xr[q] = *reinterpret_cast<const u32x4*>(P.x + (size_t)r * d_in + k);
-      else
-        xr[q] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int cc = 0; cc < 2; ++cc) aoff[cc] = (unsigned)(j * kRowBytes + (((cc * 4 + g) ^ (j & 7)) * 16));
+  const unsigned bw_lane = (unsigned)(j * kBitsRowBytes);  // + rt * 16 * kBitsRowBytes
+  const unsigned bw_swz = ((j >> 3) & 1) * 4;               // word-index xor of this lane's rows
+
+  // ---- registers ----------------------------------------------------------------------------------
+  u32x4 xv[2][NTW][2];  // [set][tile][chunk] activation B operands
+  u32x4 wr[2];
+  u32x4 br[2];
+
+  auto load_x = [&](int ks, int set) {
+    const int kc = min(ks, nsteps - 1) * kKS;
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        xv[set][i][cc] = *reinterpret_cast<const u32x4*>(xg + xoff[i] + kc + cc * 32);
   };
-  auto store_x = [&](int buf) {
-    uint16_t* dst = xs + buf * M * kXStride;
-#pragma unroll
-    for (int q = 0; q < kXPieces; ++q) {
-      const int pc = tid + q * kThreads;
-      const int r = pc >> 3, c = pc & 7;
-      if (r < M) *reinterpret_cast<u32x4*>(dst + r * kXStride + c * 8) = xr[q];
-    }
+  auto load_w = [&](int ks, int set) {
+    const int kc = min(ks, nsteps - 1) * kKS;
+    wr[set] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wg + wsrc + kc));
   };
-  // sign words: NS slots x 64 rows x 2 words
-  u32x2 br[kBitPieces];
-  auto load_bits = [&](int ks) {
+  auto store_w = [&](int buf, int set) { *lds_at<u32x4>(WS, buf * kWBytes + wdst) = wr[set]; };
+  // the sign-word piece moved at step `ks` belongs to group ks / 4 + 1, quarter ks % 4
+  auto bits_slot = [&](int ks) { return min(bslot_base + 4 * (ks & 3), NS - 1); };
+  auto load_bits = [&](int ks, int set) {
+    const int grp = min((ks >> 2) + 1, (nsteps - 1) >> 2);
+    const int widx = min(grp * 8 + bhalf * 4, wpr - 4);
+    br[set] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        a.prob[p].words[bits_slot(ks)] + (size_t)bgrow * wpr + widx));
+  };
+  auto store_bits = [&](int ks, int set) {
+    const int grp = (ks >> 2) + 1;
+    *lds_at<u32x4>(BS, (grp & 1) * bs_bytes + bits_slot(ks) * kRows * kBitsRowBytes + bdst) =
+        br[set];
+  };
+
+  f32x4 accb[NTW][kRT], accd[NTW][kRT];
 #pragma unroll
-    for (int q = 0; q < kBitPieces; ++q) {
-      const int pc = tid + q * kThreads;
-      const int s = pc >> 6, r = pc & 63;
-      const int row = min(row0 + r, d_out - 1);
-      u32x2 v = {0u, 0u};
-      if (s < NS) {
-        const uint32_t* src = P.words[s] + (size_t)row * wpr + ks * 2;
-        v[0] = src[0];
-        if (ks * 2 + 1 < wpr) v[1] = src[1];
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      accb[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accd[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // ---- prologue ------------------------------------------------------------------------------------
+#pragma unroll
+  for (int quarter = 0; quarter < 4; ++quarter) {  // sign-word group 0 straight into BS[0]
+    const int slot = bits_slot(quarter);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        a.prob[p].words[slot] + (size_t)bgrow * wpr + min(bhalf * 4, wpr - 4)));
+    *lds_at<u32x4>(BS, slot * kRows * kBitsRowBytes + bdst) = v;
+  }
+  load_x(0, 0);
+  load_x(1, 1);
+  load_w(0, 0);
+  store_w(0, 0);
+  load_w(1, 1);
+  load_w(2, 0);
+  load_bits(0, 0);
+  load_bits(1, 1);
+  lds_barrier();
+
+  // ---- main loop: two steps per iteration so each register set is fixed at compile time -------
+  auto step = [&](int ks, auto set_c) {
+    constexpr int set = decltype(set_c)::value;  // == ks & 1
+    const unsigned wbuf = (unsigned)set * kWBytes;
+    const unsigned bbuf = (unsigned)((ks >> 2) & 1) * bs_bytes;
+    const int quarter = ks & 3;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4 A[kRT];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        A[rt] = *lds_at<const u32x4>(WS, wbuf + aoff[cc] + rt * 16 * kRowBytes);
+      const unsigned wsel = bbuf + bw_lane + (unsigned)((2 * quarter + cc) ^ bw_swz) * 4;
+      u32x4 S[kRT];
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+        if (!treal[i]) break;  // the wave's remaining tiles are past the batch
+        if (tnew[i]) {
+          unsigned word[kRT];
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+            word[rt] = *lds_at<const unsigned>(BS, wsel + tslot[i] + rt * 16 * kBitsRowBytes);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) S[rt] = expand_signs(word[rt], byte_sel);
+        }
+        const u32x4 B = xv[set][i][cc];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          accb[i][rt] = mfma(A[rt], B, accb[i][rt]);
+          accd[i][rt] = mfma(S[rt], B, accd[i][rt]);
+        }
       }
-      br[q] = v;
     }
+    // commit what the next step needs (loaded two steps ago) into the other buffers
+    store_w(set ^ 1, set ^ 1);
+    store_bits(ks, set);
+    lds_barrier();
+    // issue loads: activations for step ks+2 into the set just consumed, weights and sign
+    // words two steps ahead of their commit
+    load_x(ks + 2, set);
+    load_w(ks + 3, set ^ 1);
+    load_bits(ks + 2, set);
   };
-  auto store_bits = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < kBitPieces; ++q) {
-      const int pc = tid + q * kThreads;
-      const int s = pc >> 6, r = pc & 63;
-      if (s < NS) *reinterpret_cast<u32x2*>(bs + ((buf * NS + s) * 64 + r) * 2) = br[q];
-    }
-  };
-  auto load_w = [&](int ks, u32x4* wv) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int k = ks * kKS + cc * 32;
-      if (k < d_in)
-        wv[cc] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + k));
-      else
-        wv[cc] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-
-  f32x4 accb[NT], accd[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    accb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < nsteps; ks += 2) {
+    step(ks, std::integral_constant<int, 0>{});
+    step(ks + 1, std::integral_constant<int, 1>{});
   }
 
-  u32x4 wcur[2], wnext[2];
-  load_x(0);
-  load_bits(0);
-  load_w(0, wcur);
-  store_x(0);
-  store_bits(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nsteps;
-    if (more) {
-      load_w(ks + 1, wnext);
-      load_x(ks + 1);
-      load_bits(ks + 1);
-    }
-    const uint16_t* xb = xs + buf * M * kXStride;
-    const uint32_t* bb = bs + (buf * NS * 64 + wave * 16 + j) * 2;
+  // ---- epilogue: lane holds rows 4g..4g+3 of each row tile for token j of each tile ----------
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      if (ks * kKS + cc * 32 < d_in) {
-        const u32x4 A = wcur[cc];
-        int cur = -1;
-        u32x4 S = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < NTW; ++i) {
+    const int ti = wave * NTW + i;
+    if (ti < T) {
+      const int s = a.tile_slot[ti];
+      const float al = s >= 0 ? *a.prob[p].alpha[s] : 0.f;
+      if (j < (int)a.tile_valid[ti]) {
+        const size_t ybase = (size_t)(a.tile_src[ti] + j) * d_out;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          if (i < T) {
-            const u32x4 B = *reinterpret_cast<const u32x4*>(xb + xoff[i] + cc * 32);
-            accb[i] = mfma(A, B, accb[i]);
-            const int s = a.tile_slot[i];
-            if (s >= 0) {
-              if (s != cur) {
-                S = expand_signs(bb[s * 128 + cc], byte_sel);
-                cur = s;
-              }
-              accd[i] = mfma(S, B, accd[i]);
+        for (int rt = 0; rt < kRT; ++rt) {
+          const int orow = row0 + rt * 16 + 4 * g;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = accb[i][rt][r] + al * accd[i][rt][r];
+          if (a.y_f32) {
+            float* y = reinterpret_cast<float*>(a.prob[p].y) + ybase;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (orow + r < d_out) y[orow + r] = v[r];
+          } else {
+            uint16_t* y = reinterpret_cast<uint16_t*>(a.prob[p].y) + ybase;
+            if (orow + 3 < d_out && (d_out & 3) == 0) {
+              u32x2 pk;
+              pk[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+              pk[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+              *reinterpret_cast<u32x2*>(y + orow) = pk;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (orow + r < d_out) y[orow + r] = (uint16_t)f32_to_bf16_rne(v[r]);
             }
           }
         }
       }
     }
-    if (more) {
-      store_x(buf ^ 1);
-      store_bits(buf ^ 1);
-      wcur[0] = wnext[0];
-      wcur[1] = wnext[1];
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane holds rows 4g..4g+3 (of the wave's 16) for token j of each tile --------
-  const int orow = row0 + wave * 16 + 4 * g;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    if (i < T) {
-      const int s = a.tile_slot[i];
-      const float al = s >= 0 ? *P.alpha[s] : 0.f;
-      if (j < (int)a.tile_valid[i]) {
-        const size_t ybase = (size_t)(a.tile_src[i] + j) * d_out;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = accb[i][r] + al * accd[i][r];
-        if (a.y_f32) {
-          float* y = reinterpret_cast<float*>(P.y) + ybase;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (orow + r < d_out) y[orow + r] = v[r];
-        } else {
-          uint16_t* y = reinterpret_cast<uint16_t*>(P.y) + ybase;
-          if (orow + 3 < d_out && (d_out & 3) == 0) {
-            u32x2 pk;
-            pk[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-            pk[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-            *reinterpret_cast<u32x2*>(y + orow) = pk;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (orow + r < d_out) y[orow + r] = (uint16_t)f32_to_bf16_rne(v[r]);
-          }
-        }
-      }
-    }
   }
 }
 
-template <int NT>
-hipError_t launch_nt(const StreamArgs& a, int nblocks, size_t lds, hipStream_t stream) {
+template <int NTW>
+hipError_t launch_ntw(const StreamArgs& a, int nblocks, hipStream_t stream) {
+  const size_t lds = stream_lds_bytes(a.ntiles, a.nslots);
   static bool configured = false;  // benign race: every caller sets the same value
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<NT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<NTW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(stream_kernel<NT>, dim3(nblocks), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(stream_kernel<NTW>, dim3(nblocks), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t stream_lds_bytes(int ntiles, int nslots) {
+  (void)ntiles;
+  return 2 * (size_t)kWBytes + 2 * (size_t)nslots * kRows * kBitsRowBytes;
+}
+
 hipError_t launch_stream(const StreamArgs& a, int nblocks, hipStream_t stream) {
-  const size_t lds = (size_t)2 * a.M * kXStride * 2 + (size_t)2 * a.nslots * 64 * 2 * 4;
-  if (a.ntiles <= 4) return launch_nt<4>(a, nblocks, lds, stream);
-  if (a.ntiles <= 8) return launch_nt<8>(a, nblocks, lds, stream);
-  if (a.ntiles <= 16) return launch_nt<16>(a, nblocks, lds, stream);
-  return launch_nt<kStreamMaxTiles>(a, nblocks, lds, stream);
+  if (a.ntiles < 1 || a.ntiles > kStreamMaxTiles || a.nslots < 1 || a.nslots > kMaxSlots)
+    return hipErrorInvalidValue;
+  if (a.ntiles <= kWaves) return launch_ntw<1>(a, nblocks, stream);
+  if (a.ntiles <= 2 * kWaves) return launch_ntw<2>(a, nblocks, stream);
+  return launch_ntw<3>(a, nblocks, stream);
 }
 
 }  // namespace bd

@@ -90,6 +90,12 @@ def run_matmul(case, path, out_dtype, check_delta=True):
     var_ref = [O.compress_ref(d) for d in case["deltas"]]
     w = bf16_dev(w_bits)
     x = bf16_dev(x_bits[perm])
+    if path == "stream" and d_in % 128 != 0:
+        # the streaming kernel fetches sign words 4 K-steps at a time: d_in % 128 == 0 only
+        with pytest.raises(bd.BitDeltaError) as err:
+            bd.matmul(x, w, var_gpu, offs, segv, out_dtype=out_dtype, path=path)
+        assert err.value.status == 5
+        return None
     y = bd.matmul(x, w, var_gpu, offs, segv, out_dtype=out_dtype, path=path)
     torch.cuda.synchronize()
     xf = O.bf16_bits_to_f64(x_bits)[perm]
@@ -100,9 +106,14 @@ def run_matmul(case, path, out_dtype, check_delta=True):
     assert rel.max() <= ROW_L2_TOL, f"row rel L2 {rel.max():.3e}"
     y_delta = oracle_delta_term(xf, var_ref, offs, segv, d_out, d_in)
     dres = delta_residual(y_got, y_ref, y_delta)
+    eff = path
+    if path == "auto":  # the path the library picks (streaming needs d_in % 128 == 0)
+        eff = {1: "gemv", 2: "stream", 3: "prefill"}[bd.auto_path(x.shape[0], offs, segv)]
+        if eff == "stream" and d_in % 128:
+            eff = "prefill"
     if out_dtype == "f32":
         # fp32 output: decode paths keep W_eff exact (fp32 accumulation only)
-        lim = (5e-3, 0.75) if path == "prefill" else (1e-5, 1e-2)
+        lim = (5e-3, 0.75) if eff == "prefill" else (1e-5, 1e-2)
         assert rel.max() <= lim[0], f"f32 row rel L2 {rel.max():.3e}"
         if check_delta and dres.size:
             assert dres.max() <= lim[1], f"delta residual {dres.max():.3e}"
@@ -116,12 +127,15 @@ PATH_CASES = [
     ("tiny", 16, 32, 1, 1, 0.0, ("gemv", "stream", "prefill")),
     ("m3-ragged", 70, 96, 3, 2, 0.3, ("gemv", "stream", "prefill")),
     ("m4-mixed", 200, 1056, 4, 3, 0.25, ("gemv", "stream", "prefill")),
-    ("m17", 130, 544, 17, 5, 0.1, ("stream", "prefill")),
+    ("m4-stream", 200, 1152, 4, 3, 0.25, ("gemv", "stream", "prefill")),
+    ("m10-auto", 72, 96, 10, 2, 0.2, ("auto", "prefill")),
+    ("m17", 130, 640, 17, 5, 0.1, ("stream", "prefill")),
     ("m64-14v", 192, 1024, 64, 14, 0.0, ("stream", "prefill")),
-    ("m130", 96, 2080, 130, 6, 0.2, ("stream", "prefill")),
+    ("m130", 96, 2176, 130, 6, 0.2, ("stream", "prefill")),
     ("m256-zipf", 128, 512, 256, 14, 0.0, ("stream", "prefill")),
     ("m300-chunks", 64, 256, 300, 14, 0.05, ("stream", "prefill")),
-    ("m600", 136, 320, 600, 3, 0.1, ("prefill", "stream")),
+    ("m600", 136, 384, 600, 3, 0.1, ("prefill", "stream")),
+    ("m40-base-only", 80, 256, 40, 2, 1.0, ("stream", "prefill")),
 ]
 
 
@@ -148,7 +162,7 @@ def test_identity_readback_exact():
     """x = I reads every reconstructed weight back through the product: with fp32 output the
     decode paths give fp32(w + alpha*s) exactly (one rounding), prefill bf16 of that value."""
     rng = np.random.default_rng(21)
-    d_out, d_in = 80, 64
+    d_out, d_in = 80, 128
     w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
     delta = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
     x_bits = WL.f32_to_bf16_bits(np.eye(d_in, dtype=np.float32))
