@@ -215,7 +215,7 @@ def run_decode(args, torch, bd, config):
 
     cpu = None
     if not args.no_cpu_baseline:
-        sample = [l for l in linears if l[0] in ("k", "v", "q")] or linears
+        sample = [l for l in linears if l[0] in ("q", "k", "v", "o")] or linears
         cpu = cpu_baseline_decode(torch, config, sample, scales, perm, offs, segv, m, total_elems,
                                   nvar)
 
