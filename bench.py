@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=5, choices=(2, 3, 4, 5))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--path", default="auto", choices=("auto", "gemv", "stream", "split", "prefill"),
+                   help="decode kernel family (auto: what the library picks)")
     return p.parse_args()
 
 
@@ -182,16 +184,19 @@ def run_decode(args, torch, bd, config):
         for L in blk:
             L.x = WL.gpu_normal_bf16(torch, (m, L.d_in), 1.0, WL.substream_seed(config, b, L.name, "x"))
             L.y = torch.empty((m, L.d_out), dtype=torch.bfloat16, device="cuda")
+    # one workspace for the whole step (blocks run one after another on one stream)
+    ws_bytes = max(sum(bd.matmul_workspace_bytes(m, L.d_in, args.path) for L in blk) for blk in layers)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     def step(timer=None):
-        # plan (host) + one grouped launch per block
+        # plan (host) + one grouped call per block (split path: activation prologue + main kernel)
         _, o, s = bd.plan_segments(ids, nvar)
         for blk in layers:
             probs = [(L.x, L.w, L.y, L.variants) for L in blk]
             if timer:
                 timer.start()
-            bd.matmul_grouped(probs, o, s)
+            bd.matmul_grouped(probs, o, s, path=args.path, workspace=ws)
             if timer:
                 timer.stop()
 
@@ -211,7 +216,7 @@ def run_decode(args, torch, bd, config):
     avg_launch_s = kern_ms / launches / 1e3
     achieved = bytes_launch / avg_launch_s / 1e9
     total_elems = sum(L.d_out * L.d_in for blk in layers for L in blk)
-    path = bd.auto_path(m, offs, segv)
+    path = bd.auto_path(m, offs, segv) if args.path == "auto" else bd.PATHS[args.path]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -233,12 +238,13 @@ def run_decode(args, torch, bd, config):
         "config": {"workload": names[config], "config_index": config, "tokens_per_step": m,
                    "segments": [int(v) for v in np.diff(offs)], "active_variants": n_active,
                    "launches_per_step": launches // args.steps,
-                   "kernel_path": {1: "gemv", 2: "stream", 3: "prefill"}[path],
+                   "kernel_path": {1: "gemv", 2: "stream", 3: "prefill", 4: "split"}[path],
                    "parallelism": "single GPU"},
         "hbm_gbs_step": bytes_launch * len(layers) / (ms_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "stream_kernel" if path == 2 else "gemv_kernel",
+                     "kernel": {1: "gemv_kernel", 2: "stream_kernel",
+                                4: "split_act_kernel + split_kernel"}.get(path, "?"),
                      "bytes_per_launch": bytes_launch, "avg_launch_us": avg_launch_s * 1e6},
         "compress": {"matrices": len(comp.pairs), "bytes": comp_bytes, "ms": comp_ms,
                      "gbs": comp_bytes / (comp_ms / 1e3) / 1e9,

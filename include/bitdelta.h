@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define BITDELTA_ABI_VERSION 1
+#define BITDELTA_ABI_VERSION 2
 #define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
 #define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
 #define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
@@ -45,7 +45,7 @@ typedef enum {
   BITDELTA_ERR_INVALID_ARG = 1, /* null pointer, negative size, unknown enum value            */
   BITDELTA_ERR_SHAPE = 2,       /* d_in not a multiple of 32, inconsistent segments           */
   BITDELTA_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned (words: 4-byte)    */
-  BITDELTA_ERR_WORKSPACE = 4,   /* workspace smaller than bitdelta_compress_workspace_bytes   */
+  BITDELTA_ERR_WORKSPACE = 4,   /* workspace smaller than the matching *_workspace_bytes query */
   BITDELTA_ERR_UNSUPPORTED = 5, /* a size beyond what the kernels handle                      */
   BITDELTA_ERR_HIP = 6          /* the HIP runtime reported an error while enqueueing         */
 } bitdelta_status;
@@ -59,8 +59,10 @@ typedef enum { BITDELTA_OUT_BF16 = 0, BITDELTA_OUT_F32 = 1 } bitdelta_out_dtype;
 typedef enum {
   BITDELTA_PATH_AUTO = 0,
   BITDELTA_PATH_GEMV = 1,    /* fp32 reconstruction in registers, VALU; M <= 4                 */
-  BITDELTA_PATH_STREAM = 2,  /* decode: split base/sign bf16 MFMA, each weight byte read once  */
-  BITDELTA_PATH_PREFILL = 3  /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
+  BITDELTA_PATH_STREAM = 2,  /* decode: base and sign sums both as bf16 MFMA; no workspace     */
+  BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
+  BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp8 MFMA on an exact
+                              * two-term fp8 split of x; needs workspace                       */
 } bitdelta_path;
 
 /* One compressed variant of one weight matrix: the output of bitdelta_compress. */
@@ -135,6 +137,15 @@ bitdelta_status bitdelta_plan_segments(const int32_t* token_variant, int64_t M,
                                        int32_t* num_segments);
 
 /*
+ * bitdelta_matmul_workspace_bytes — device workspace one linear (one problem) of a matmul call
+ * on `path` needs, for a batch of M tokens and input width d_in (a multiple of 256 bytes; 0 when
+ * the path needs none).  AUTO reports what the path AUTO would pick for M needs.  A grouped call
+ * needs the sum over its problems.  The SPLIT path writes each token's activations there as two
+ * fp8 terms (2 * d_in bytes) plus a scale code (4 bytes); M = 0 or invalid arguments give 0.
+ */
+size_t bitdelta_matmul_workspace_bytes(int64_t M, int64_t d_in, int32_t path);
+
+/*
  * bitdelta_matmul — the fused reconstruct-and-multiply of the BitDelta post ("Serving
  * architecture", conceptual fused linear): for every token t in segment s with variant
  * v = seg_variant[s],
@@ -149,26 +160,36 @@ bitdelta_status bitdelta_plan_segments(const int32_t* token_variant, int64_t M,
  *   seg_offsets  [host] int32 [num_segments + 1], 0 = first <= ... <= last = M.
  *   seg_variant  [host] int32 [num_segments], each in [-1, num_variants).
  *   y            [dev] out [M][d_out], bf16 (round-to-nearest-even) or float32 per y_dtype.
- * M = 0 is a no-op (x and y may then be NULL).  Errors: INVALID_ARG, SHAPE, ALIGNMENT,
- * UNSUPPORTED, HIP.  y must not alias any input.
+ *   workspace    [dev] at least bitdelta_matmul_workspace_bytes(M, d_in, BITDELTA_PATH_AUTO)
+ *                bytes, 256-byte aligned (may be NULL when that is 0); scratch owned by the
+ *                caller, used by the kernels this call enqueues, contents afterwards unspecified.
+ *                Calls in flight at the same time need separate workspaces.
+ * M = 0 is a no-op (x, y and workspace may then be NULL).  Errors: INVALID_ARG, SHAPE,
+ * ALIGNMENT, WORKSPACE, UNSUPPORTED, HIP.  y must not alias any input or the workspace.
  */
 bitdelta_status bitdelta_matmul(const void* x, const void* w_base, int64_t M, int64_t d_out,
                                 int64_t d_in, const bitdelta_variant* variants,
                                 int32_t num_variants, const int32_t* seg_offsets,
                                 const int32_t* seg_variant, int32_t num_segments, void* y,
-                                int32_t y_dtype, bitdelta_stream stream);
+                                int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                                bitdelta_stream stream);
 
 /*
  * bitdelta_matmul_grouped — bitdelta_matmul over up to BITDELTA_MAX_PROBLEMS independent
  * linears that share one token segmentation (e.g. the seven linears of a decoder block for
  * one decode batch), enqueued as few launches as possible so small matrices share the GPU.
- * `path` selects the kernel family (bitdelta_path); AUTO picks by M and segment sizes.
+ * `path` selects the kernel family (bitdelta_path); AUTO picks by M (GEMV for M <= 4, SPLIT
+ * for M <= 256, PREFILL above; SPLIT and STREAM fall back to PREFILL when d_in is not a multiple
+ * of 128 or a sign-word pointer is not 16-byte aligned, while a forced path reports
+ * UNSUPPORTED).  `workspace` must hold the sum over the problems of
+ * bitdelta_matmul_workspace_bytes(M, d_in_p, path), 256-byte aligned.
  * Errors as bitdelta_matmul, checked for every problem before anything is enqueued.
  */
 bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_t num_problems,
                                         int64_t M, const int32_t* seg_offsets,
                                         const int32_t* seg_variant, int32_t num_segments,
-                                        int32_t y_dtype, int32_t path, bitdelta_stream stream);
+                                        int32_t y_dtype, int32_t path, void* workspace,
+                                        size_t workspace_bytes, bitdelta_stream stream);
 
 /* The kernel family bitdelta_matmul_grouped's AUTO would pick for this batch (a
  * bitdelta_path value), or -1 for invalid segments.  Host only. */

@@ -15,12 +15,13 @@ import numpy as np
 __all__ = [
     "BitDeltaError", "lib", "abi_version", "sign_words", "compress_workspace_bytes",
     "compress", "plan_segments", "matmul", "matmul_grouped", "auto_path", "PATHS",
+    "matmul_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitdelta.so")
 
-PATHS = {"auto": 0, "gemv": 1, "stream": 2, "prefill": 3}
+PATHS = {"auto": 0, "gemv": 1, "stream": 2, "prefill": 3, "split": 4}
 _OUT = {"bf16": 0, "f32": 1}
 MAX_VARIANTS = 64
 MAX_PROBLEMS = 8
@@ -74,11 +75,16 @@ def _lib():
         L.bitdelta_matmul.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_Variant),
                                       ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
-                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
         L.bitdelta_matmul_grouped.restype = ctypes.c_int
         L.bitdelta_matmul_grouped.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32,
                                               ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
-                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_matmul_workspace_bytes.restype = ctypes.c_size_t
+        L.bitdelta_matmul_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
+                                                      ctypes.c_int32]
         L.bitdelta_auto_path.restype = ctypes.c_int32
         L.bitdelta_auto_path.argtypes = [ctypes.c_int64, _i32p, _i32p, ctypes.c_int32]
         _LIB = L
@@ -159,6 +165,23 @@ def plan_segments(token_variant, num_variants: int):
     return perm[:m].copy(), offs[:n + 1].copy(), segv[:n].copy()
 
 
+def matmul_workspace_bytes(m: int, d_in: int, path="auto") -> int:
+    """Device workspace one linear of a matmul call on ``path`` needs (bytes, 0 if none)."""
+    return int(_lib().bitdelta_matmul_workspace_bytes(m, d_in, PATHS[path]))
+
+
+def _workspace(workspace, need, device):
+    """(pointer, bytes) of the caller's workspace tensor, or of a fresh one when None."""
+    import torch
+    if workspace is None:
+        if need == 0:
+            return None, 0, None
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
 def auto_path(m: int, seg_offsets, seg_variant) -> int:
     o, op = _i32(seg_offsets)
     v, vp = _i32(seg_variant)
@@ -176,9 +199,12 @@ def _variants_array(variants):
     return arr
 
 
-def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="auto", stream=None):
+def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="auto", stream=None,
+                   workspace=None):
     """Fused y = x (W_base + alpha_v sign_v)^T for several linears sharing one segmentation.
-    ``problems``: list of (x, w_base, y, variants) with variants a list of (words, alpha)."""
+    ``problems``: list of (x, w_base, y, variants) with variants a list of (words, alpha).
+    ``workspace``: device tensor of at least the summed matmul_workspace_bytes (allocated here
+    when None)."""
     if not 1 <= len(problems) <= MAX_PROBLEMS:
         raise ValueError("1..8 problems per call")
     offs, offs_p = _i32(seg_offsets)
@@ -197,14 +223,17 @@ def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="a
         parr[i].num_variants = len(variants)
         if x.shape[0] != m or y.shape[0] != m:
             raise ValueError("x and y must have seg_offsets[-1] rows")
+    need = sum(matmul_workspace_bytes(m, int(w.shape[1]), path) for _, w, _, _ in problems)
+    ws_ptr, ws_bytes, ws = _workspace(workspace, need, problems[0][1].device)
     _check(_lib().bitdelta_matmul_grouped(parr, len(problems), m, offs_p, segv_p, segv.size,
-                                          _OUT[out_dtype], PATHS[path], _stream(stream)),
+                                          _OUT[out_dtype], PATHS[path], ws_ptr, ws_bytes,
+                                          _stream(stream)),
            "bitdelta_matmul_grouped")
     return [p[2] for p in problems]
 
 
 def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf16", path="auto",
-           stream=None):
+           stream=None, workspace=None):
     """Fused y = x (W_base + alpha_v sign_v)^T over a token batch grouped by variant."""
     import torch
     if y is None:
@@ -212,15 +241,17 @@ def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf1
                         dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
     if path != "auto":
         matmul_grouped([(x, w_base, y, variants)], seg_offsets, seg_variant, out_dtype, path,
-                       stream)
+                       stream, workspace)
         return y
     offs, offs_p = _i32(seg_offsets)
     segv, segv_p = _i32(seg_variant)
     varr = _variants_array(variants)
+    ws_ptr, ws_bytes, ws = _workspace(
+        workspace, matmul_workspace_bytes(int(x.shape[0]), int(w_base.shape[1])), x.device)
     _check(_lib().bitdelta_matmul(
         _dev(x, "torch.bfloat16", "x"), _dev(w_base, "torch.bfloat16", "w_base"),
         int(x.shape[0]), int(w_base.shape[0]), int(w_base.shape[1]), varr, len(variants),
         offs_p, segv_p, segv.size,
         _dev(y, "torch.bfloat16" if out_dtype == "bf16" else "torch.float32", "y"),
-        _OUT[out_dtype], _stream(stream)), "bitdelta_matmul")
+        _OUT[out_dtype], ws_ptr, ws_bytes, _stream(stream)), "bitdelta_matmul")
     return y

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <utility>
 #include <vector>
 
 #include "../../include/bitdelta.h"
@@ -62,11 +63,17 @@ bitdelta_status check_problem(const bitdelta_problem& p, int64_t M,
 
 int pick_path(int64_t M) {
   if (M <= 4) return BITDELTA_PATH_GEMV;
-  if (M <= bd::kStreamMaxM) return BITDELTA_PATH_STREAM;
+  if (M <= bd::kSplitMaxM) return BITDELTA_PATH_SPLIT;
   return BITDELTA_PATH_PREFILL;
 }
 
-// The streaming kernel reads sign words 16 bytes (4 K steps) per row at a time.
+size_t workspace_for(int64_t M, int64_t d_in, int path) {
+  if (M <= 0 || d_in <= 0 || M >= kMaxDim || d_in >= kMaxDim) return 0;
+  if (path == BITDELTA_PATH_AUTO) path = pick_path(M);
+  return path == BITDELTA_PATH_SPLIT ? bd::split_workspace_bytes(M, d_in) : 0;
+}
+
+// The streaming kernels read sign words 16 bytes (4 K steps) per row at a time.
 bool stream_eligible(const bitdelta_problem* probs, int np, const std::vector<Segment>& segs) {
   for (int p = 0; p < np; ++p) {
     if (probs[p].d_in % 128 != 0) return false;
@@ -183,6 +190,117 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
       if (r != BITDELTA_OK) return r;
     }
     t0 = t1;
+  }
+  return BITDELTA_OK;
+}
+
+// ---- split-activation decode: chunks of <= 256 tokens, <= 24 variant tiles, <= 16 variants ---
+bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
+                          const std::vector<Segment>& segs, int y_f32, void* workspace,
+                          hipStream_t st) {
+  // workspace: per problem, fp8 hi/lo activations then the per-token scale codes
+  bd::SplitActArgs act;
+  memset(&act, 0, sizeof(act));
+  const int Mp = (int)((M + 15) / 16 * 16);
+  act.Mp = Mp;
+  std::vector<unsigned char*> xb(np), xq(np);
+  std::vector<int*> xs(np);
+  size_t off = 0;
+  for (int p = 0; p < np; ++p) {
+    unsigned char* base = static_cast<unsigned char*>(workspace) + off;
+    const size_t qbytes = ((size_t)Mp * 2 * (size_t)probs[p].d_in + 255) / 256 * 256;
+    xb[p] = base;
+    xq[p] = base + qbytes;
+    xs[p] = reinterpret_cast<int*>(base + 2 * qbytes);
+    off += bd::split_workspace_bytes(M, probs[p].d_in);
+    act.x[p] = static_cast<const uint16_t*>(probs[p].x);
+    act.xb[p] = xb[p];
+    act.xq[p] = xq[p];
+    act.xscale[p] = xs[p];
+    act.d_in[p] = (int)probs[p].d_in;
+  }
+  bitdelta_status r = map_hip(bd::launch_split_act(act, (int)M, np, st));
+  if (r != BITDELTA_OK) return r;
+
+  // problems with longer rows first, so the longest workgroups do not form the tail
+  std::vector<int> order(np);
+  for (int p = 0; p < np; ++p) order[p] = p;
+  for (int i = 1; i < np; ++i)
+    for (int k = i; k > 0 && probs[order[k]].d_in > probs[order[k - 1]].d_in; --k)
+      std::swap(order[k], order[k - 1]);
+
+  struct Unit {
+    int tok, n, variant;
+  };
+  std::vector<Unit> units;
+  for (const Segment& s : segs)
+    for (int r0 = 0; r0 < s.len; r0 += 16) units.push_back({s.begin + r0, s.len - r0 < 16 ? s.len - r0 : 16, s.variant});
+  size_t u0 = 0;
+  while (u0 < units.size()) {
+    const int t_begin = units[u0].tok;
+    std::vector<int> slot_var;
+    int ntiles = 0;
+    size_t u1 = u0;
+    while (u1 < units.size()) {
+      const Unit& u = units[u1];
+      if (u.tok + u.n - t_begin > bd::kSplitMaxM) break;
+      if (u.variant >= 0) {
+        if (ntiles == bd::kSplitMaxTiles) break;
+        bool have = false;
+        for (int v : slot_var) have = have || v == u.variant;
+        if (!have && (int)slot_var.size() == bd::kMaxSlots) break;
+        if (!have) slot_var.push_back(u.variant);
+        ++ntiles;
+      }
+      ++u1;
+    }
+    const int t_end = units[u1 - 1].tok + units[u1 - 1].n;
+    bd::SplitArgs a;
+    memset(&a, 0, sizeof(a));
+    a.M = t_end - t_begin;
+    a.tok0 = t_begin;
+    a.Mp = Mp;
+    a.ntiles = ntiles;
+    a.nslots = (int)slot_var.size();
+    a.y_f32 = y_f32;
+    int ti = 0;
+    for (size_t i = u0; i < u1; ++i) {
+      const Unit& u = units[i];
+      if (u.variant < 0) continue;
+      int slot = 0;
+      for (int q = 0; q < (int)slot_var.size(); ++q)
+        if (slot_var[q] == u.variant) slot = q;
+      a.tile_slot[ti] = (int8_t)slot;
+      a.tile_valid[ti] = (uint8_t)u.n;
+      a.tile_src[ti] = (int16_t)(u.tok - t_begin);
+      ++ti;
+      for (int t = u.tok - t_begin; t < u.tok - t_begin + u.n; ++t)
+        a.has_delta[t >> 5] |= 1u << (t & 31);
+    }
+    for (int p0 = 0; p0 < np; p0 += bd::kMaxProblems) {
+      const int pn = np - p0 < bd::kMaxProblems ? np - p0 : bd::kMaxProblems;
+      a.nprob = pn;
+      for (int q = 0; q < pn; ++q) {
+        const int p = order[p0 + q];
+        const bitdelta_problem& P = probs[p];
+        bd::SplitProblem& S = a.prob[q];
+        S.x = reinterpret_cast<const uint16_t*>(xb[p]);
+        S.xq = xq[p];
+        S.xscale = xs[p];
+        S.w = static_cast<const uint16_t*>(P.w_base);
+        S.y = static_cast<char*>(P.y) + (size_t)t_begin * P.d_out * (y_f32 ? 4 : 2);
+        S.d_out = (int)P.d_out;
+        S.d_in = (int)P.d_in;
+        S.nblocks = (int)((P.d_out + bd::kSplitRows - 1) / bd::kSplitRows);
+        for (int s = 0; s < (int)slot_var.size(); ++s) {
+          S.words[s] = P.variants[slot_var[s]].sign_words;
+          S.alpha[s] = P.variants[slot_var[s]].alpha;
+        }
+      }
+      r = map_hip(bd::launch_split(a, st));
+      if (r != BITDELTA_OK) return r;
+    }
+    u0 = u1;
   }
   return BITDELTA_OK;
 }
@@ -325,14 +443,20 @@ int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t*
   return pick_path(M);
 }
 
+size_t bitdelta_matmul_workspace_bytes(int64_t M, int64_t d_in, int32_t path) {
+  if (path < BITDELTA_PATH_AUTO || path > BITDELTA_PATH_SPLIT) return 0;
+  return workspace_for(M, d_in, path);
+}
+
 bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_t num_problems,
                                         int64_t M, const int32_t* seg_offsets,
                                         const int32_t* seg_variant, int32_t num_segments,
-                                        int32_t y_dtype, int32_t path, bitdelta_stream stream) {
+                                        int32_t y_dtype, int32_t path, void* workspace,
+                                        size_t workspace_bytes, bitdelta_stream stream) {
   if (!problems || num_problems <= 0 || num_problems > BITDELTA_MAX_PROBLEMS)
     return BITDELTA_ERR_INVALID_ARG;
   if (y_dtype != BITDELTA_OUT_BF16 && y_dtype != BITDELTA_OUT_F32) return BITDELTA_ERR_INVALID_ARG;
-  if (path < BITDELTA_PATH_AUTO || path > BITDELTA_PATH_PREFILL) return BITDELTA_ERR_INVALID_ARG;
+  if (path < BITDELTA_PATH_AUTO || path > BITDELTA_PATH_SPLIT) return BITDELTA_ERR_INVALID_ARG;
   std::vector<Segment> segs;
   bitdelta_status s = check_segments(M, seg_offsets, seg_variant, num_segments, &segs);
   if (s != BITDELTA_OK) return s;
@@ -344,15 +468,27 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
   const bool explicit_path = path != BITDELTA_PATH_AUTO;
   if (path == BITDELTA_PATH_AUTO) path = pick_path(M);
   if (path == BITDELTA_PATH_GEMV && M > 4) return BITDELTA_ERR_UNSUPPORTED;
-  if (path == BITDELTA_PATH_STREAM && !stream_eligible(problems, num_problems, segs)) {
+  bool eligible = stream_eligible(problems, num_problems, segs);
+  if (path == BITDELTA_PATH_SPLIT)  // activation layouts are addressed with 31-bit offsets
+    for (int p = 0; p < num_problems; ++p)
+      eligible = eligible && (M + 15) / 16 * 16 * 2 * problems[p].d_in < (int64_t(1) << 31);
+  if ((path == BITDELTA_PATH_STREAM || path == BITDELTA_PATH_SPLIT) && !eligible) {
     if (explicit_path) return BITDELTA_ERR_UNSUPPORTED;
     path = BITDELTA_PATH_PREFILL;
+  }
+  if (path == BITDELTA_PATH_SPLIT) {
+    size_t need = 0;
+    for (int p = 0; p < num_problems; ++p) need += workspace_for(M, problems[p].d_in, path);
+    if (!workspace || workspace_bytes < need) return BITDELTA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BITDELTA_ERR_ALIGNMENT;
   }
   const int y_f32 = y_dtype == BITDELTA_OUT_F32;
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (path) {
     case BITDELTA_PATH_GEMV: return run_gemv(problems, num_problems, M, segs, y_f32, st);
     case BITDELTA_PATH_STREAM: return run_stream(problems, num_problems, segs, y_f32, st);
+    case BITDELTA_PATH_SPLIT:
+      return run_split(problems, num_problems, M, segs, y_f32, workspace, st);
     default: return run_prefill(problems, num_problems, segs, y_f32, st);
   }
 }
@@ -361,7 +497,8 @@ bitdelta_status bitdelta_matmul(const void* x, const void* w_base, int64_t M, in
                                 int64_t d_in, const bitdelta_variant* variants,
                                 int32_t num_variants, const int32_t* seg_offsets,
                                 const int32_t* seg_variant, int32_t num_segments, void* y,
-                                int32_t y_dtype, bitdelta_stream stream) {
+                                int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                                bitdelta_stream stream) {
   bitdelta_problem p;
   p.x = x;
   p.w_base = w_base;
@@ -371,7 +508,7 @@ bitdelta_status bitdelta_matmul(const void* x, const void* w_base, int64_t M, in
   p.variants = variants;
   p.num_variants = num_variants;
   return bitdelta_matmul_grouped(&p, 1, M, seg_offsets, seg_variant, num_segments, y_dtype,
-                                 BITDELTA_PATH_AUTO, stream);
+                                 BITDELTA_PATH_AUTO, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -97,4 +97,46 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Decode with the sign product on fp4 x fp8 MFMA (activations split into two exact fp8 terms
+// by a prologue kernel into caller workspace).  Needs d_in % 128 == 0 and 16-byte aligned sign
+// words.  One launch serves a token range of at most kSplitMaxM tokens (16 dense tiles) with at
+// most kSplitMaxTiles 16-token variant tiles and kMaxSlots distinct variants.
+constexpr int kSplitMaxM = 256;
+constexpr int kSplitMaxTiles = 24;
+constexpr int kSplitRows = 64;
+
+struct SplitProblem {
+  const uint16_t* x;          // bf16 activations in base-operand order (prologue layout)
+  const unsigned char* xq;    // fp8 hi/lo in sign-operand order (prologue layout)
+  const int* xscale;          // [Mp] E8M0 code of the hi term (lo: code - 4)
+  const uint16_t* w;
+  void* y;
+  int d_out, d_in;
+  int nblocks, pad_;   // 64-row blocks of this linear
+  const uint32_t* words[kMaxSlots];
+  const float* alpha[kMaxSlots];
+};
+
+struct SplitArgs {
+  SplitProblem prob[kMaxProblems];
+  int nprob, M, ntiles, nslots, y_f32;
+  int tok0, Mp, pad_;                    // first token of this launch; token stride of the layouts
+  uint32_t has_delta[kSplitMaxM / 32];  // bit t: token t belongs to a variant (not the base)
+  int8_t tile_slot[kSplitMaxTiles];     // slot of the tile's variant
+  uint8_t tile_valid[kSplitMaxTiles];   // real tokens in the tile (1..16)
+  int16_t tile_src[kSplitMaxTiles];     // first token of the tile
+};
+hipError_t launch_split(const SplitArgs& a, hipStream_t stream);  // grid from nblocks
+
+struct SplitActArgs {
+  const uint16_t* x[kMaxProblems];     // bf16 [M][d_in] row-major (the caller's activations)
+  unsigned char* xb[kMaxProblems];     // out: bf16 in base-operand order
+  unsigned char* xq[kMaxProblems];     // out: fp8 hi/lo in sign-operand order
+  int* xscale[kMaxProblems];           // out: [M] scale codes
+  int d_in[kMaxProblems];
+  int Mp, pad_;                        // token stride of the layouts (M rounded up to 16)
+};
+hipError_t launch_split_act(const SplitActArgs& a, int M, int nprob, hipStream_t stream);
+size_t split_workspace_bytes(int64_t M, int64_t d_in);  // per linear, multiple of 256
+
 }  // namespace bd

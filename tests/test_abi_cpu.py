@@ -37,7 +37,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.abi_version() == 1
+    assert bd.abi_version() == 2
     for s in range(7):
         assert L.bitdelta_status_string(s)
     assert L.bitdelta_status_string(99) == b"unknown status"
@@ -92,7 +92,8 @@ def test_compress_validation():
     assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE, ws - 8) == WORKSPACE
 
 
-def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None):
+def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None, ws=FAKE,
+            ws_bytes=1 << 40):
     o = np.ascontiguousarray(offs, dtype=np.int32)
     v = np.ascontiguousarray(segv, dtype=np.int32)
     op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -102,13 +103,14 @@ def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None)
         varr[i].sign_words, varr[i].alpha = wd, al
     if path is None:
         return L.bitdelta_matmul(x, w, m, d_out, d_in, varr, len(variants), op, vp, v.size, y,
-                                 y_dtype, None)
+                                 y_dtype, ws, ws_bytes, None)
     prob = (bd._Problem * 1)()
     prob[0].x, prob[0].w_base, prob[0].y = x, w, y
     prob[0].d_out, prob[0].d_in = d_out, d_in
     prob[0].variants = ctypes.cast(varr, ctypes.POINTER(bd._Variant))
     prob[0].num_variants = len(variants)
-    return L.bitdelta_matmul_grouped(prob, 1, m, op, vp, v.size, y_dtype, path, None)
+    return L.bitdelta_matmul_grouped(prob, 1, m, op, vp, v.size, y_dtype, path, ws, ws_bytes,
+                                     None)
 
 
 def test_matmul_validation():
@@ -138,6 +140,9 @@ def test_matmul_validation():
     assert call(y_dtype=7) == INVALID
     assert call(path=9) == INVALID
     assert call(path=1) == UNSUPPORTED            # the GEMV path takes at most 4 tokens
+    # d_in = 64 is not a multiple of 128: the decode paths refuse it when forced
+    assert call(path=2) == UNSUPPORTED
+    assert call(path=4) == UNSUPPORTED
     # an unused variant may be absent
     assert call(m=0, offs=[0, 0, 0]) == OK         # empty batch: nothing enqueued
     assert call(m=0, offs=[0], segv=[]) == OK
@@ -145,10 +150,40 @@ def test_matmul_validation():
     assert call(m=0, offs=[0], segv=[], w=None) == INVALID
 
 
+def test_split_workspace_validation():
+    V = [(FAKE, FAKE), (FAKE + 256, FAKE + 512)]
+    need = bd.matmul_workspace_bytes(8, 128)
+    good = dict(x=FAKE, w=FAKE, m=8, d_out=64, d_in=128, variants=V, offs=[0, 3, 8], segv=[0, 1],
+                y=FAKE, path=4)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return _matmul(**a)
+
+    assert call(ws=None, ws_bytes=0) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 16, ws_bytes=need) == ALIGN
+    assert call(path=0, ws=None, ws_bytes=0) == WORKSPACE   # AUTO picks SPLIT for 8 tokens
+    assert call(m=0, offs=[0, 0, 0], ws=None, ws_bytes=0) == OK
+
+
+def test_matmul_workspace_bytes():
+    # per token (M rounded up to 16): a bf16 copy and the fp8 hi + lo terms (2 bytes per element
+    # each) plus one int32 scale code, each region rounded up to 256 bytes
+    assert bd.matmul_workspace_bytes(256, 8192) == 2 * 256 * 2 * 8192 + 1024
+    assert bd.matmul_workspace_bytes(5, 128, "split") == 2 * 16 * 256 + 256
+    assert bd.matmul_workspace_bytes(4, 8192) == 0            # AUTO -> GEMV, no workspace
+    assert bd.matmul_workspace_bytes(300, 8192) == 0          # AUTO -> PREFILL
+    assert bd.matmul_workspace_bytes(64, 8192, "stream") == 0
+    assert bd.matmul_workspace_bytes(0, 8192, "split") == 0
+    assert bd.matmul_workspace_bytes(64, 8192, "split") % 256 == 0
+
+
 def test_auto_path_choice():
     assert bd.auto_path(1, [0, 1], [0]) == 1
     assert bd.auto_path(4, [0, 2, 4], [0, 3]) == 1
-    assert bd.auto_path(64, [0, 64], [0]) == 2
-    assert bd.auto_path(256, [0, 100, 256], [-1, 5]) == 2
+    assert bd.auto_path(64, [0, 64], [0]) == 4
+    assert bd.auto_path(256, [0, 100, 256], [-1, 5]) == 4
     assert bd.auto_path(8192, [0, 2048, 4096, 6144, 8192], [0, 1, 2, 3]) == 3
     assert bd.auto_path(8, [0, 9], [0]) == -1

@@ -90,8 +90,8 @@ def run_matmul(case, path, out_dtype, check_delta=True):
     var_ref = [O.compress_ref(d) for d in case["deltas"]]
     w = bf16_dev(w_bits)
     x = bf16_dev(x_bits[perm])
-    if path == "stream" and d_in % 128 != 0:
-        # the streaming kernel fetches sign words 4 K-steps at a time: d_in % 128 == 0 only
+    if path in ("stream", "split") and d_in % 128 != 0:
+        # the streaming kernels fetch sign words 4 K-steps at a time: d_in % 128 == 0 only
         with pytest.raises(bd.BitDeltaError) as err:
             bd.matmul(x, w, var_gpu, offs, segv, out_dtype=out_dtype, path=path)
         assert err.value.status == 5
@@ -108,8 +108,8 @@ def run_matmul(case, path, out_dtype, check_delta=True):
     dres = delta_residual(y_got, y_ref, y_delta)
     eff = path
     if path == "auto":  # the path the library picks (streaming needs d_in % 128 == 0)
-        eff = {1: "gemv", 2: "stream", 3: "prefill"}[bd.auto_path(x.shape[0], offs, segv)]
-        if eff == "stream" and d_in % 128:
+        eff = {1: "gemv", 2: "stream", 3: "prefill", 4: "split"}[bd.auto_path(x.shape[0], offs, segv)]
+        if eff in ("stream", "split") and d_in % 128:
             eff = "prefill"
     if out_dtype == "f32":
         # fp32 output: decode paths keep W_eff exact (fp32 accumulation only)
@@ -124,18 +124,20 @@ def run_matmul(case, path, out_dtype, check_delta=True):
 
 PATH_CASES = [
     # (name, d_out, d_in, M, variants, base_frac, paths)
-    ("tiny", 16, 32, 1, 1, 0.0, ("gemv", "stream", "prefill")),
-    ("m3-ragged", 70, 96, 3, 2, 0.3, ("gemv", "stream", "prefill")),
-    ("m4-mixed", 200, 1056, 4, 3, 0.25, ("gemv", "stream", "prefill")),
-    ("m4-stream", 200, 1152, 4, 3, 0.25, ("gemv", "stream", "prefill")),
+    ("tiny", 16, 32, 1, 1, 0.0, ("gemv", "stream", "split", "prefill")),
+    ("m3-ragged", 70, 96, 3, 2, 0.3, ("gemv", "stream", "split", "prefill")),
+    ("m4-mixed", 200, 1056, 4, 3, 0.25, ("gemv", "stream", "split", "prefill")),
+    ("m4-stream", 200, 1152, 4, 3, 0.25, ("gemv", "stream", "split", "prefill")),
     ("m10-auto", 72, 96, 10, 2, 0.2, ("auto", "prefill")),
-    ("m17", 130, 640, 17, 5, 0.1, ("stream", "prefill")),
-    ("m64-14v", 192, 1024, 64, 14, 0.0, ("stream", "prefill")),
-    ("m130", 96, 2176, 130, 6, 0.2, ("stream", "prefill")),
-    ("m256-zipf", 128, 512, 256, 14, 0.0, ("stream", "prefill")),
-    ("m300-chunks", 64, 256, 300, 14, 0.05, ("stream", "prefill")),
-    ("m600", 136, 384, 600, 3, 0.1, ("prefill", "stream")),
-    ("m40-base-only", 80, 256, 40, 2, 1.0, ("stream", "prefill")),
+    ("m12-auto-split", 72, 384, 12, 2, 0.2, ("auto", "split")),
+    ("m17", 130, 640, 17, 5, 0.1, ("stream", "split", "prefill")),
+    ("m64-14v", 192, 1024, 64, 14, 0.0, ("stream", "split", "prefill")),
+    ("m130", 96, 2176, 130, 6, 0.2, ("stream", "split", "prefill")),
+    ("m256-zipf", 128, 512, 256, 14, 0.0, ("stream", "split", "prefill")),
+    ("m300-chunks", 64, 256, 300, 14, 0.05, ("stream", "split", "prefill")),
+    ("m600", 136, 384, 600, 3, 0.1, ("prefill", "stream", "split")),
+    ("m40-base-only", 80, 256, 40, 2, 1.0, ("stream", "split", "prefill")),
+    ("m200-62v-chunks", 66, 384, 200, 62, 0.0, ("split", "stream")),
 ]
 
 
@@ -153,7 +155,7 @@ def test_matmul_paths(case, out_dtype):
 
 def test_config1_all_paths():
     c = WL.config1()
-    for path in ("auto", "gemv", "stream", "prefill"):
+    for path in ("auto", "gemv", "stream", "split", "prefill"):
         for out in ("bf16", "f32"):
             run_matmul(c, path, out)
 
@@ -171,7 +173,7 @@ def test_identity_readback_exact():
     weff = O.reconstruct_ref(O.bf16_bits_to_f64(w_bits), ref_words, ref_alpha)  # fp64 exact
     want_f32 = weff.astype(np.float32).T
     want_bf16 = O.bf16_bits_to_f64(WL.f32_to_bf16_bits(weff.astype(np.float32))).T
-    for path in ("stream", "prefill"):
+    for path in ("stream", "split", "prefill"):
         y = bd.matmul(bf16_dev(x_bits), bf16_dev(w_bits), [(words, alpha)], [0, d_in], [0],
                       out_dtype="f32", path=path)
         got = y.cpu().numpy()
@@ -203,7 +205,7 @@ def test_zero_base_isolates_delta():
          "deltas": [rng.laplace(0, 4e-4, size=(d_out, d_in)).astype(np.float32) for _ in range(2)],
          "x": WL.f32_to_bf16_bits(rng.normal(size=(m, d_in)).astype(np.float32)),
          "token_variant": rng.integers(0, 2, size=m).astype(np.int32)}
-    for path in ("stream", "prefill"):
+    for path in ("stream", "split", "prefill"):
         run_matmul(c, path, "f32")
     c["x"], c["token_variant"] = c["x"][:3], c["token_variant"][:3]
     run_matmul(c, "gemv", "f32")
@@ -216,7 +218,7 @@ def test_zero_delta_and_base_only_tokens():
          "deltas": [np.zeros((d_out, d_in), np.float32)],
          "x": WL.f32_to_bf16_bits(rng.normal(size=(m, d_in)).astype(np.float32)),
          "token_variant": np.where(np.arange(m) % 3 == 0, -1, 0).astype(np.int32)}
-    for path in ("stream", "prefill"):
+    for path in ("stream", "split", "prefill"):
         y, y_ref, *_ = run_matmul(c, path, "f32", check_delta=False)
 
 
@@ -234,7 +236,7 @@ def test_batch_invariance_and_repeatability():
     var_gpu = gpu_compress(c["deltas"])
     w = bf16_dev(c["w"])
     x = bf16_dev(c["x"][perm])
-    for path in ("stream", "prefill"):
+    for path in ("stream", "split", "prefill"):
         y1 = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path=path)
         y2 = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path=path)
         assert torch.equal(y1, y2)
@@ -255,13 +257,53 @@ def test_grouped_matches_single():
     v1, v2 = gpu_compress(c1["deltas"]), gpu_compress(d2)
     xa, wa = bf16_dev(c1["x"][perm]), bf16_dev(c1["w"])
     xb, wb = bf16_dev(x2[perm]), bf16_dev(w2)
-    ya = torch.empty((48, 200), dtype=torch.float32, device="cuda")
-    yb = torch.empty((48, 72), dtype=torch.float32, device="cuda")
-    bd.matmul_grouped([(xa, wa, ya, v1), (xb, wb, yb, v2)], offs, segv, out_dtype="f32",
-                      path="stream")
-    sa = bd.matmul(xa, wa, v1, offs, segv, out_dtype="f32", path="stream")
-    sb = bd.matmul(xb, wb, v2, offs, segv, out_dtype="f32", path="stream")
-    assert torch.equal(ya, sa) and torch.equal(yb, sb)
     ref_b = O.matmul_ref(O.bf16_bits_to_f64(x2)[perm], O.bf16_bits_to_f64(w2),
                          [O.compress_ref(d) for d in d2], offs, segv)
-    assert row_rel_l2(yb.cpu().numpy().astype(np.float64), ref_b).max() <= 1e-5
+    for path in ("stream", "split"):
+        ya = torch.empty((48, 200), dtype=torch.float32, device="cuda")
+        yb = torch.empty((48, 72), dtype=torch.float32, device="cuda")
+        bd.matmul_grouped([(xa, wa, ya, v1), (xb, wb, yb, v2)], offs, segv, out_dtype="f32",
+                          path=path)
+        sa = bd.matmul(xa, wa, v1, offs, segv, out_dtype="f32", path=path)
+        sb = bd.matmul(xb, wb, v2, offs, segv, out_dtype="f32", path=path)
+        assert torch.equal(ya, sa) and torch.equal(yb, sb), path
+        assert row_rel_l2(yb.cpu().numpy().astype(np.float64), ref_b).max() <= 1e-5, path
+
+
+def test_split_activation_scales():
+    """The split path scales each token by its own power of two: tokens spanning 1e-30 .. 1e30,
+    an all-zero token and a token whose elements span 2^-40 .. 2^20 stay exact-class."""
+    rng = np.random.default_rng(51)
+    d_out, d_in, m = 64, 384, 7
+    g = rng.normal(size=(m, d_in))
+    g[0] *= 1e-30
+    g[1] *= 1e-3
+    g[3] *= 1e3
+    g[4] *= 1e30
+    g[5] = 0.0
+    g[6] *= 2.0 ** rng.integers(-40, 21, size=d_in)
+    c = {"w": WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32)),
+         "deltas": [rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32) for _ in range(2)],
+         "x": WL.f32_to_bf16_bits(g.astype(np.float32)),
+         "token_variant": np.array([0, 1, 0, 1, 0, 1, 0], np.int32)}
+    y, y_ref, *_ = run_matmul(c, "split", "f32", check_delta=False)
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    zero_row = int(np.where(np.all(g == 0.0, axis=1))[0][0])
+    perm, *_ = bd.plan_segments(c["token_variant"], 2)
+    assert np.all(got[int(np.where(perm == zero_row)[0][0])] == 0.0)
+
+
+def test_split_workspace_reuse_and_errors():
+    c = WL.linear_case(seed=61, d_out=96, d_in=512, m=40, num_variants=3)
+    perm, offs, segv = bd.plan_segments(c["token_variant"], 3)
+    var_gpu = gpu_compress(c["deltas"])
+    w, x = bf16_dev(c["w"]), bf16_dev(c["x"][perm])
+    need = bd.matmul_workspace_bytes(40, 512, "split")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y1 = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path="split", workspace=ws)
+    y2 = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path="split", workspace=ws)
+    assert torch.equal(y1, y2)
+    with pytest.raises(bd.BitDeltaError) as err:
+        bd.matmul(x, w, var_gpu, offs, segv, path="split", workspace=ws[: need - 256])
+    assert err.value.status == 4
