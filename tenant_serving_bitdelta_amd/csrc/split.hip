@@ -244,10 +244,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
     const int ti_raw = wave * NS + i;
     const int ti = max(0, min(ti_raw, T - 1));  // T == 0: a batch of base-model tokens only
     const int valid = a.tile_valid[ti];
-    // lanes past the tile's tokens read a neighbour token (their column is never stored)
+    // lanes past the tile's tokens read zeros without touching memory
     const int tok = a.tok0 + max(0, min(a.tile_src[ti] + j, M - 1));
-    (void)valid;
-    qoff[i] = (unsigned)g * mp16 + (unsigned)tok * 16;
+    qoff[i] = (ti_raw < T && j < valid) ? (unsigned)g * mp16 + (unsigned)tok * 16 : kOob;
     sc_hi[i] = P.xscale[tok];
     sc_lo[i] = sc_hi[i] - 4;
     const int s = a.tile_slot[ti];
