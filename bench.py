@@ -78,10 +78,13 @@ def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nva
                                            out=dbuf[:d_out * d_in])
                 words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device=dev)
                 alpha = torch.empty(1, dtype=torch.float32, device=dev)
+                nt = bd.sign_words_t128(d_out, d_in)
+                tiled = torch.empty(nt, dtype=torch.int32, device=dev) if nt > 0 else None
                 compress_timer.start()
-                bd.compress(delta, words, alpha, workspace=ws)
-                compress_timer.stop(4 * d_out * d_in + d_out * d_in // 8 + 4)
-                L.variants.append((words, alpha))
+                bd.compress(delta, words, alpha, workspace=ws, tiled=tiled)
+                # reads Delta once, writes the row-major words, the tiled copy and alpha
+                compress_timer.stop(4 * d_out * d_in + (2 if nt > 0 else 1) * (d_out * d_in // 8) + 4)
+                L.variants.append((words, alpha, tiled))
             blk.append(L)
         layers.append(blk)
         log(f"[setup] block {b + 1}/{blocks} built and compressed")

@@ -22,6 +22,11 @@
  *     r * (d_in / 32) + k / 32, least-significant bit first; bit 1 means +1, bit 0 means -1.
  *     The byte image of these words equals the BitDelta post's packing of eight sign bits per
  *     int8 ("Infrastructure details", delta storage format).  sign(+0) = sign(-0) = +1.
+ *   - Tiled sign words (optional second copy, for the SPLIT decode path; d_in % 128 == 0):
+ *     rows are grouped in blocks of 128 and columns in steps of 128; the 4 words of one row and
+ *     one step sit at word ((r / 128) * (d_in / 128) + c / 4) * 512 + (r % 128) * 4 + c % 4 for
+ *     row-major word (r, c), so each (block, step) is one contiguous 2 KiB chunk.  The last
+ *     block is padded to 128 rows; padding words are never read for output rows < d_out.
  *   - bf16 tensors are passed as `const void*` holding IEEE bfloat16 values, row-major.
  *   - d_in must be a multiple of 32 (one word per 32 elements of a row).
  */
@@ -35,7 +40,7 @@
 extern "C" {
 #endif
 
-#define BITDELTA_ABI_VERSION 2
+#define BITDELTA_ABI_VERSION 3
 #define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
 #define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
 #define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
@@ -62,13 +67,14 @@ typedef enum {
   BITDELTA_PATH_STREAM = 2,  /* decode: base and sign sums both as bf16 MFMA; no workspace     */
   BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
   BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp8 MFMA on an exact
-                              * two-term fp8 split of x; needs workspace                       */
+                              * two-term fp8 split of x; needs workspace and tiled sign words  */
 } bitdelta_path;
 
 /* One compressed variant of one weight matrix: the output of bitdelta_compress. */
 typedef struct {
-  const uint32_t* sign_words; /* [dev] d_out * d_in / 32 words, layout above, 4-byte aligned */
-  const float* alpha;         /* [dev] one float32: the per-matrix scale                      */
+  const uint32_t* sign_words;      /* [dev] d_out * d_in / 32 words, row-major, 4-byte aligned */
+  const uint32_t* sign_words_t128; /* [dev] tiled copy (layout above), 16-byte aligned, or NULL */
+  const float* alpha;              /* [dev] one float32: the per-matrix scale                  */
 } bitdelta_variant;
 
 /* One linear layer of a grouped matmul: every problem of a call sees the same token batch
@@ -93,6 +99,10 @@ const char* bitdelta_status_string(int status);
  * not a positive multiple of 32 or d_out is negative. */
 int64_t bitdelta_sign_words(int64_t d_out, int64_t d_in);
 
+/* Number of uint32 words of the tiled sign copy of a d_out x d_in matrix
+ * (ceil(d_out / 128) * 128 * d_in / 32), or -1 if d_in is not a positive multiple of 128. */
+int64_t bitdelta_sign_words_t128(int64_t d_out, int64_t d_in);
+
 /* Device workspace bytes bitdelta_compress needs for this shape (fp64 partial sums). */
 size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
 
@@ -103,6 +113,9 @@ size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
  *
  *   delta       [dev] float32 [d_out][d_in], 16-byte aligned, finite values.  Read only.
  *   sign_words  [dev] out: uint32 [d_out][d_in/32] (layout above), 4-byte aligned.
+ *   sign_words_t128 [dev] out, optional (NULL = not written): the same bits in the tiled
+ *               layout above, bitdelta_sign_words_t128 words, 16-byte aligned; needs
+ *               d_in % 128 == 0 (else SHAPE).
  *   alpha       [dev] out: one float32, the fp64 sum of |Delta| (fixed summation order, so
  *               repeated calls are bit-identical) divided by n and rounded once to float32.
  *   workspace   [dev] at least bitdelta_compress_workspace_bytes(d_out, d_in) bytes,
@@ -112,8 +125,8 @@ size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
  * The buffers must not overlap.
  */
 bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
-                                  uint32_t* sign_words, float* alpha, void* workspace,
-                                  size_t workspace_bytes, bitdelta_stream stream);
+                                  uint32_t* sign_words, uint32_t* sign_words_t128, float* alpha,
+                                  void* workspace, size_t workspace_bytes, bitdelta_stream stream);
 
 /*
  * bitdelta_plan_segments — group a token batch by variant (host only, O(M), no device work).
@@ -179,9 +192,10 @@ bitdelta_status bitdelta_matmul(const void* x, const void* w_base, int64_t M, in
  * linears that share one token segmentation (e.g. the seven linears of a decoder block for
  * one decode batch), enqueued as few launches as possible so small matrices share the GPU.
  * `path` selects the kernel family (bitdelta_path); AUTO picks by M (GEMV for M <= 4, SPLIT
- * for M <= 256, PREFILL above; SPLIT and STREAM fall back to PREFILL when d_in is not a multiple
- * of 128 or a sign-word pointer is not 16-byte aligned, while a forced path reports
- * UNSUPPORTED).  `workspace` must hold the sum over the problems of
+ * for M <= 256, PREFILL above).  SPLIT needs d_in % 128 == 0 and the tiled sign words of every
+ * variant the batch uses; STREAM needs d_in % 128 == 0 and 16-byte aligned sign words.  When
+ * AUTO's choice does not apply it falls back SPLIT -> STREAM -> PREFILL; a forced path that does
+ * not apply reports UNSUPPORTED.  `workspace` must hold the sum over the problems of
  * bitdelta_matmul_workspace_bytes(M, d_in_p, path), 256-byte aligned.
  * Errors as bitdelta_matmul, checked for every problem before anything is enqueued.
  */

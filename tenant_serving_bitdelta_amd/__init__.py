@@ -15,7 +15,7 @@ import numpy as np
 __all__ = [
     "BitDeltaError", "lib", "abi_version", "sign_words", "compress_workspace_bytes",
     "compress", "plan_segments", "matmul", "matmul_grouped", "auto_path", "PATHS",
-    "matmul_workspace_bytes",
+    "matmul_workspace_bytes", "sign_words_t128",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,8 @@ class BitDeltaError(RuntimeError):
 
 
 class _Variant(ctypes.Structure):
-    _fields_ = [("sign_words", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
+    _fields_ = [("sign_words", ctypes.c_void_p), ("sign_words_t128", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p)]
 
 
 class _Problem(ctypes.Structure):
@@ -67,7 +68,9 @@ def _lib():
         L.bitdelta_compress.restype = ctypes.c_int
         L.bitdelta_compress.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                        ctypes.c_size_t, ctypes.c_void_p]
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_sign_words_t128.restype = ctypes.c_int64
+        L.bitdelta_sign_words_t128.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.bitdelta_plan_segments.restype = ctypes.c_int
         L.bitdelta_plan_segments.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
                                              _i32p, _i32p]
@@ -130,21 +133,28 @@ def sign_words(d_out: int, d_in: int) -> int:
     return int(_lib().bitdelta_sign_words(d_out, d_in))
 
 
+def sign_words_t128(d_out: int, d_in: int) -> int:
+    """Words of the tiled sign copy (128-row blocks x 128-column steps), -1 if d_in % 128."""
+    return int(_lib().bitdelta_sign_words_t128(d_out, d_in))
+
+
 def compress_workspace_bytes(d_out: int, d_in: int) -> int:
     return int(_lib().bitdelta_compress_workspace_bytes(d_out, d_in))
 
 
-def compress(delta, words, alpha, workspace=None, stream=None):
+def compress(delta, words, alpha, workspace=None, stream=None, tiled=None):
     """alpha = mean|delta| and packed sign bits of one float32 [d_out, d_in] matrix.
-    ``words``: int32 tensor [d_out, d_in // 32] (uint32 bit patterns), ``alpha``: float32 [1]."""
+    ``words``: int32 tensor [d_out, d_in // 32] (uint32 bit patterns), ``alpha``: float32 [1],
+    ``tiled``: optional int32 tensor of sign_words_t128(d_out, d_in) words for the tiled copy."""
     import torch
     d_out, d_in = delta.shape
     if workspace is None:
         workspace = torch.empty(max(compress_workspace_bytes(d_out, d_in), 8) // 8,
                                 dtype=torch.float64, device=delta.device)
+    tptr = None if tiled is None else _dev(tiled, "torch.int32", "tiled sign words")
     _check(_lib().bitdelta_compress(
         _dev(delta, "torch.float32", "delta"), d_out, d_in, _dev(words, "torch.int32", "words"),
-        _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
+        tptr, _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)), "bitdelta_compress")
     return words, alpha
 
@@ -189,13 +199,16 @@ def auto_path(m: int, seg_offsets, seg_variant) -> int:
 
 
 def _variants_array(variants):
+    """variants: list of (words, alpha) or (words, alpha, tiled_words) (or None for unused)."""
     arr = (_Variant * max(len(variants), 1))()
     for i, item in enumerate(variants):
         if item is None:
             continue
-        words, alpha = item
+        words, alpha = item[0], item[1]
         arr[i].sign_words = _dev(words, "torch.int32", "sign words")
         arr[i].alpha = _dev(alpha, "torch.float32", "alpha")
+        if len(item) > 2 and item[2] is not None:
+            arr[i].sign_words_t128 = _dev(item[2], "torch.int32", "tiled sign words")
     return arr
 
 

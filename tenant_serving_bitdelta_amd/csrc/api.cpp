@@ -83,6 +83,24 @@ bool stream_eligible(const bitdelta_problem* probs, int np, const std::vector<Se
   return true;
 }
 
+// The split path reads the tiled sign words and addresses its activation layouts and the tiled
+// words with 31-bit offsets.
+bool split_eligible(const bitdelta_problem* probs, int np, int64_t M,
+                    const std::vector<Segment>& segs) {
+  for (int p = 0; p < np; ++p) {
+    const bitdelta_problem& P = probs[p];
+    if (P.d_in % 128 != 0) return false;
+    if ((M + 15) / 16 * 16 * 2 * P.d_in >= (int64_t(1) << 31)) return false;
+    if ((P.d_out + 127) / 128 * 128 * (P.d_in / 8) >= (int64_t(1) << 31)) return false;
+    for (const Segment& s : segs) {
+      if (s.variant < 0) continue;
+      const uint32_t* t = P.variants[s.variant].sign_words_t128;
+      if (!t || !aligned(t, 16)) return false;
+    }
+  }
+  return true;
+}
+
 // ---- GEMV: one launch per linear ----------------------------------------------------------
 bitdelta_status run_gemv(const bitdelta_problem* probs, int np, int64_t M,
                          const std::vector<Segment>& segs, int y_f32, hipStream_t st) {
@@ -238,12 +256,13 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
   size_t u0 = 0;
   while (u0 < units.size()) {
     const int t_begin = units[u0].tok;
+    const int tok_base = t_begin / 16 * 16;   // launches cover whole 16-token blocks
     std::vector<int> slot_var;
     int ntiles = 0;
     size_t u1 = u0;
     while (u1 < units.size()) {
       const Unit& u = units[u1];
-      if (u.tok + u.n - t_begin > bd::kSplitMaxM) break;
+      if (u.tok + u.n - tok_base > bd::kSplitMaxM) break;
       if (u.variant >= 0) {
         if (ntiles == bd::kSplitMaxTiles) break;
         bool have = false;
@@ -257,8 +276,9 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
     const int t_end = units[u1 - 1].tok + units[u1 - 1].n;
     bd::SplitArgs a;
     memset(&a, 0, sizeof(a));
-    a.M = t_end - t_begin;
-    a.tok0 = t_begin;
+    a.tok_base = tok_base;
+    a.lo = t_begin - tok_base;
+    a.hi = t_end - tok_base;
     a.Mp = Mp;
     a.ntiles = ntiles;
     a.nslots = (int)slot_var.size();
@@ -272,9 +292,9 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
         if (slot_var[q] == u.variant) slot = q;
       a.tile_slot[ti] = (int8_t)slot;
       a.tile_valid[ti] = (uint8_t)u.n;
-      a.tile_src[ti] = (int16_t)(u.tok - t_begin);
+      a.tile_src[ti] = (int16_t)(u.tok - tok_base);
       ++ti;
-      for (int t = u.tok - t_begin; t < u.tok - t_begin + u.n; ++t)
+      for (int t = u.tok - tok_base; t < u.tok - tok_base + u.n; ++t)
         a.has_delta[t >> 5] |= 1u << (t & 31);
     }
     for (int p0 = 0; p0 < np; p0 += bd::kMaxProblems) {
@@ -284,16 +304,16 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
         const int p = order[p0 + q];
         const bitdelta_problem& P = probs[p];
         bd::SplitProblem& S = a.prob[q];
-        S.x = reinterpret_cast<const uint16_t*>(xb[p]);
+        S.x = xb[p];
         S.xq = xq[p];
         S.xscale = xs[p];
         S.w = static_cast<const uint16_t*>(P.w_base);
-        S.y = static_cast<char*>(P.y) + (size_t)t_begin * P.d_out * (y_f32 ? 4 : 2);
+        S.y = P.y;
         S.d_out = (int)P.d_out;
         S.d_in = (int)P.d_in;
         S.nblocks = (int)((P.d_out + bd::kSplitRows - 1) / bd::kSplitRows);
         for (int s = 0; s < (int)slot_var.size(); ++s) {
-          S.words[s] = P.variants[slot_var[s]].sign_words;
+          S.words[s] = P.variants[slot_var[s]].sign_words_t128;
           S.alpha[s] = P.variants[slot_var[s]].alpha;
         }
       }
@@ -384,23 +404,29 @@ int64_t bitdelta_sign_words(int64_t d_out, int64_t d_in) {
   return d_out * (d_in / 32);
 }
 
+int64_t bitdelta_sign_words_t128(int64_t d_out, int64_t d_in) {
+  if (d_out < 0 || d_in <= 0 || d_in % 128 != 0 || d_out >= kMaxDim || d_in >= kMaxDim) return -1;
+  return (d_out + 127) / 128 * 128 * (d_in / 32);
+}
+
 size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in) {
   if (d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || d_out >= kMaxDim || d_in >= kMaxDim) return 0;
   return (size_t)bd::compress_grid(d_out * d_in) * sizeof(double);
 }
 
 bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
-                                  uint32_t* sign_words, float* alpha, void* workspace,
-                                  size_t workspace_bytes, bitdelta_stream stream) {
+                                  uint32_t* sign_words, uint32_t* sign_words_t128, float* alpha,
+                                  void* workspace, size_t workspace_bytes, bitdelta_stream stream) {
   if (!delta || !sign_words || !alpha || !workspace) return BITDELTA_ERR_INVALID_ARG;
   if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim)
     return BITDELTA_ERR_INVALID_ARG;
   if (d_in % 32 != 0) return BITDELTA_ERR_SHAPE;
+  if (sign_words_t128 && d_in % 128 != 0) return BITDELTA_ERR_SHAPE;
   if (!aligned(delta, 16) || !aligned(sign_words, 4) || !aligned(alpha, 4) ||
-      !aligned(workspace, 8))
+      !aligned(workspace, 8) || !aligned(sign_words_t128, 16))
     return BITDELTA_ERR_ALIGNMENT;
   if (workspace_bytes < bitdelta_compress_workspace_bytes(d_out, d_in)) return BITDELTA_ERR_WORKSPACE;
-  return map_hip(bd::launch_compress(delta, d_out * d_in, sign_words, alpha,
+  return map_hip(bd::launch_compress(delta, d_out * d_in, d_in, sign_words, sign_words_t128, alpha,
                                      static_cast<double*>(workspace),
                                      static_cast<hipStream_t>(stream)));
 }
@@ -468,11 +494,11 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
   const bool explicit_path = path != BITDELTA_PATH_AUTO;
   if (path == BITDELTA_PATH_AUTO) path = pick_path(M);
   if (path == BITDELTA_PATH_GEMV && M > 4) return BITDELTA_ERR_UNSUPPORTED;
-  bool eligible = stream_eligible(problems, num_problems, segs);
-  if (path == BITDELTA_PATH_SPLIT)  // activation layouts are addressed with 31-bit offsets
-    for (int p = 0; p < num_problems; ++p)
-      eligible = eligible && (M + 15) / 16 * 16 * 2 * problems[p].d_in < (int64_t(1) << 31);
-  if ((path == BITDELTA_PATH_STREAM || path == BITDELTA_PATH_SPLIT) && !eligible) {
+  if (path == BITDELTA_PATH_SPLIT && !split_eligible(problems, num_problems, M, segs)) {
+    if (explicit_path) return BITDELTA_ERR_UNSUPPORTED;
+    path = BITDELTA_PATH_STREAM;
+  }
+  if (path == BITDELTA_PATH_STREAM && !stream_eligible(problems, num_problems, segs)) {
     if (explicit_path) return BITDELTA_ERR_UNSUPPORTED;
     path = BITDELTA_PATH_PREFILL;
   }

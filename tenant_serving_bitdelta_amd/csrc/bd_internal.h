@@ -29,8 +29,10 @@ __device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
 // Compress (two passes)
 // ---------------------------------------------------------------------------------------------
 int compress_grid(int64_t n);  // number of pass-1 workgroups (= fp64 partials) for n elements
-hipError_t launch_compress(const float* delta, int64_t n, uint32_t* words, float* alpha,
-                           double* partials, hipStream_t stream);
+// words: row-major [d_out][d_in/32]; tiled: optional copy in the 128-row tiled layout (NULL for
+// none; needs d_in % 128 == 0).
+hipError_t launch_compress(const float* delta, int64_t n, int64_t d_in, uint32_t* words,
+                           uint32_t* tiled, float* alpha, double* partials, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
 // Matmul kernels
@@ -106,25 +108,27 @@ constexpr int kSplitMaxTiles = 24;
 constexpr int kSplitRows = 64;
 
 struct SplitProblem {
-  const uint16_t* x;          // bf16 activations in base-operand order (prologue layout)
+  const unsigned char* x;     // bf16 activations in base-operand order (prologue layout)
   const unsigned char* xq;    // fp8 hi/lo in sign-operand order (prologue layout)
   const int* xscale;          // [Mp] E8M0 code of the hi term (lo: code - 4)
   const uint16_t* w;
-  void* y;
+  void* y;                    // [M][d_out] of the whole call
   int d_out, d_in;
-  int nblocks, pad_;   // 64-row blocks of this linear
-  const uint32_t* words[kMaxSlots];
+  int nblocks, pad_;          // 64-row blocks of this linear
+  const uint32_t* words[kMaxSlots];  // tiled sign words (128-row layout)
   const float* alpha[kMaxSlots];
 };
 
 struct SplitArgs {
   SplitProblem prob[kMaxProblems];
-  int nprob, M, ntiles, nslots, y_f32;
-  int tok0, Mp, pad_;                    // first token of this launch; token stride of the layouts
-  uint32_t has_delta[kSplitMaxM / 32];  // bit t: token t belongs to a variant (not the base)
+  int nprob, ntiles, nslots, y_f32;
+  int tok_base;                          // first token of this launch's 16-token blocks
+  int lo, hi;                            // tokens [tok_base + lo, tok_base + hi) are this launch's
+  int Mp;                                // token count of the layouts (call's M rounded up to 16)
+  uint32_t has_delta[kSplitMaxM / 32];  // bit t: token tok_base + t belongs to a variant
   int8_t tile_slot[kSplitMaxTiles];     // slot of the tile's variant
   uint8_t tile_valid[kSplitMaxTiles];   // real tokens in the tile (1..16)
-  int16_t tile_src[kSplitMaxTiles];     // first token of the tile
+  int16_t tile_src[kSplitMaxTiles];     // first token of the tile, relative to tok_base
 };
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream);  // grid from nblocks
 

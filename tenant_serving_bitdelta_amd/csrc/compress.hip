@@ -10,6 +10,13 @@
 // the word.  |Delta| is accumulated in fp64 per lane and reduced per workgroup into one fp64
 // partial.  Pass 2 sums the partials in a fixed order and rounds sum/n once to float32, so the
 // result is identical from run to run (no atomics anywhere).
+//
+// Optionally pass 1 also writes a second copy of the sign words in the tiled layout the
+// split-activation decode kernel streams: for every block of 128 rows and every 128-column step,
+// the 4 words of each of the 128 rows lie in one contiguous 2 KiB chunk,
+//   tiled word ((r / 128) * (d_in / 128) + c / 4) * 512 + (r % 128) * 4 + c % 4  <-  word (r, c),
+// so a block's sign words for one step are read as whole cache lines.  Rows past d_out in the
+// last block are not written.
 #include "bd_internal.h"
 
 namespace bd {
@@ -41,6 +48,8 @@ __device__ __forceinline__ double wave_sum(double v) {
 __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restrict__ delta,
                                                           int64_t n4,
                                                           uint32_t* __restrict__ words,
+                                                          uint32_t* __restrict__ tiled,
+                                                          int64_t wpr,
                                                           double* __restrict__ partials) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -70,7 +79,14 @@ __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restri
       part |= __shfl_xor(part, 2);
       part |= __shfl_xor(part, 4);
       // n is a multiple of 32, so the 8 lanes of a word are all in range or all out of range.
-      if ((lane & 7) == 0 && ok[u]) words[i >> 3] = part;
+      if ((lane & 7) == 0 && ok[u]) {
+        const int64_t w = i >> 3;
+        words[w] = part;
+        if (tiled) {
+          const int64_t r = w / wpr, c = w - r * wpr;
+          tiled[((r >> 7) * (wpr >> 2) + (c >> 2)) * 512 + (r & 127) * 4 + (c & 3)] = part;
+        }
+      }
     }
   }
 
@@ -113,11 +129,12 @@ int compress_grid(int64_t n) {
   return (int)g;
 }
 
-hipError_t launch_compress(const float* delta, int64_t n, uint32_t* words, float* alpha,
-                           double* partials, hipStream_t stream) {
+hipError_t launch_compress(const float* delta, int64_t n, int64_t d_in, uint32_t* words,
+                           uint32_t* tiled, float* alpha, double* partials, hipStream_t stream) {
   const int grid = compress_grid(n);
   hipLaunchKernelGGL(compress_pass1, dim3(grid), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const f32x4*>(delta), n / 4, words, partials);
+                     reinterpret_cast<const f32x4*>(delta), n / 4, words, tiled, d_in / 32,
+                     partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compress_pass2, dim3(1), dim3(kThreads), 0, stream, partials, grid,

@@ -30,11 +30,11 @@
 // Work split.  A workgroup (8 waves, two per SIMD) owns 64 output rows of one linear.  Wave w
 // owns dense tiles w and w+8 (base sum, ND per wave) and variant tiles [w*NS, w*NS+NS) (sign
 // sum).  The K loop walks d_in in steps of 128:
-//   * W_base (64 rows x 128, 16 KiB) is copied by direct global->LDS loads (16 bytes per lane)
-//     four steps ahead into a 5-stage ring (64 KiB in flight per CU to cover HBM latency),
-//     laid out so each MFMA A operand is 1 KiB of consecutive lanes (conflict-free reads);
-//   * the sign words of every active variant (16 bytes per row per step) are copied the same
-//     way, two steps (32 bytes per row) at a time, into a 2-group ring;
+//   * W_base (64 rows x 128, 16 KiB) and the sign words of every active variant (the tiled
+//     copy: 64 rows x 16 B = 1 KiB contiguous per variant and step) are copied by direct
+//     global->LDS loads (16 bytes per lane, whole cache lines) three steps ahead into a 4-stage
+//     ring; W_base's 16-byte chunks are XOR-swizzled by row so MFMA operand reads are
+//     conflict-free;
 //   * each wave's activations (bf16 for dense tiles, fp8 hi/lo for variant tiles) go straight
 //     from memory into MFMA B-operand registers, reloaded for the next step right after use;
 //   * one workgroup barrier per step; before it each wave waits only for its copies that the
@@ -55,18 +55,11 @@ constexpr int kRows = kSplitRows;        // 64 output rows per workgroup
 constexpr int kRT = kRows / 16;          // row tiles
 constexpr int kKS = 128;                 // k per step
 constexpr unsigned kWStage = kRows * kKS * 2;        // 16 KiB of W_base per step
-#ifndef SPLIT_WSTAGES
-#define SPLIT_WSTAGES 5
-#endif
-#ifndef SPLIT_DMA_AUX
-#define SPLIT_DMA_AUX 0
-#endif
-constexpr int kWStages = SPLIT_WSTAGES;             // W ring depth; copies run kWStages-1 ahead
-constexpr int kWAhead = kWStages - 1;
-constexpr unsigned kSBase = kWStages * kWStage;      // sign-word ring after the W ring
-constexpr unsigned kSSlotG = kRows * 32;             // one slot, one two-step group: 64 rows x 32 B
-constexpr unsigned kSGroup = kMaxSlots * kSSlotG;    // one group, every slot
-constexpr unsigned kLdsBytes = kSBase + 2 * kSGroup; // 144 KiB with 5 W stages
+constexpr unsigned kSSlot = kRows * 16;              // one variant's sign words, one step: 1 KiB
+constexpr unsigned kStage = kWStage + kMaxSlots * kSSlot;  // W_base + signs of one step: 32 KiB
+constexpr int kStages = 4;                           // LDS ring; copies run kStages-1 steps ahead
+constexpr int kAhead = kStages - 1;
+constexpr unsigned kLdsBytes = kStages * kStage;     // 128 KiB
 constexpr int kEStride = kRows + 4;                  // floats per token row of the epilogue buffer
 static_assert(kSplitMaxM * kEStride * 4 <= (int)kLdsBytes, "epilogue buffer exceeds LDS");
 
@@ -107,7 +100,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
 // (MUBUF) form is used rather than the global one so the compiler's wait-count tracking of the
 // other loads stays exact; the copies themselves are waited for explicitly before barriers.
 __device__ __forceinline__ void dma16(rsrc_t r, unsigned voff, unsigned char* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, SPLIT_DMA_AUX);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
 }
 
 // 16 bytes from a raw buffer; an offset at or past kOob reads as zero without touching memory.
@@ -153,28 +146,23 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
   }
   if (p < 0) return;  // this XCD's list is shorter than the longest one
   const SplitProblem& P = a.prob[p];
-  const uint16_t* __restrict__ xg = P.x;
-  const unsigned char* __restrict__ qg = P.xq;
-  const uint16_t* __restrict__ wg = P.w;
   const int d_in = P.d_in, d_out = P.d_out;
   const int row0 = rb * kRows;
-  const int M = a.M;
   const int T = a.ntiles;
   const int nslots = a.nslots;
-  const int wpr = d_in >> 5;
   const int nsteps = d_in / kKS;
+  const int lo_tok = a.lo, hi_tok = a.hi;      // valid tokens, relative to a.tok_base
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
 
-  // ---- direct copies this wave issues ----------------------------------------------------------
-  // Offsets are relative to row row0 of the block; rows past d_out are clamped to d_out - 1.
+  // ---- direct copies (global -> LDS), kAhead steps ahead, into stage s % kStages ---------------
   // W_base: copy b = 2*wave + u (of 16) moves rows 4b..4b+3 of the block for one step, 256 bytes
   // each, so every 4 consecutive lanes read 64 contiguous bytes.  Lane L writes LDS slot
   // (row 4b + L/16, 16-byte position L%16) and fetches 16-byte column chunk position ^ (row%16):
   // the XOR swizzle keeps the MFMA operand reads below conflict-free.
-  const rsrc_t wrs = make_rsrc(wg + (size_t)row0 * d_in);
+  const rsrc_t wrs = make_rsrc(P.w + (size_t)row0 * d_in);
   unsigned woff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -182,59 +170,48 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
     const int row = min(row0 + rl, d_out - 1) - row0;
     woff[u] = (unsigned)((row * d_in + 8 * ((lane & 15) ^ (rl & 15))) * 2);
   }
-  // sign words of a two-step group: copy c = wave + 8u (c < 2 * nslots) moves rows 32h..32h+31
-  // (h = c % 2) of slot c / 2; lane L takes row 32h + L/2, step 2G + L%2 (16 bytes), so every two
-  // lanes read 32 contiguous bytes.  LDS per slot and group: [64 rows][2 steps][16 B].
-  const int sq = lane & 1;  // step of the group this lane copies
-  rsrc_t srs[4];
-  unsigned soff[4], sdst[4];
-  bool sreal[4];
+  // sign words (tiled layout): the 64 rows of this block for one step are 1 KiB contiguous at
+  // word ((row0 / 128) * nsteps + s) * 512 + (row0 % 128) * 4; copy of slot wave + 8u.
+  rsrc_t srs[2];
+  bool sreal[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = wave + kWaves * u;
-    sreal[u] = c < 2 * nslots;
-    const int cc = sreal[u] ? c : 0;
-    const int slot = cc >> 1, h = cc & 1;
-    srs[u] = make_rsrc(a.prob[p].words[slot] + (size_t)row0 * wpr);
-    soff[u] = (unsigned)((min(row0 + 32 * h + (lane >> 1), d_out - 1) - row0) * wpr * 4);
-    sdst[u] = kSBase + (unsigned)slot * kSSlotG + (unsigned)h * 1024;
+  for (int u = 0; u < 2; ++u) {
+    const int slot = wave + kWaves * u;
+    sreal[u] = slot < nslots;
+    srs[u] = make_rsrc(P.words[sreal[u] ? slot : 0]);
   }
-  auto issue_w = [&](int s) {
+  const unsigned soff = (unsigned)((((row0 >> 7) * nsteps) * 512 + (row0 & 127) * 4) * 4) + lane * 16;
+  auto issue = [&](int s) {  // copies for step s
     if (s < nsteps) {
-      unsigned char* dst = smem + (unsigned)(s % kWStages) * kWStage;
+      unsigned char* st = smem + (unsigned)(s % kStages) * kStage;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        dma16(wrs, woff[u] + (unsigned)s * (kKS * 2), dst + (2 * wave + u) * 1024);
+        dma16(wrs, woff[u] + (unsigned)s * (kKS * 2), st + (2 * wave + u) * 1024);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (sreal[u])
+          dma16(srs[u], soff + (unsigned)s * 2048, st + kWStage + (wave + kWaves * u) * kSSlot);
     }
   };
-  auto issue_signs = [&](int grp) {  // steps 2*grp, 2*grp + 1 (the second clamped at the end)
-    if (2 * grp >= nsteps) return;
-    const unsigned ring = (unsigned)(grp & 1) * kSGroup;
-    const unsigned step = (unsigned)min(2 * grp + sq, nsteps - 1);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (sreal[u]) dma16(srs[u], soff[u] + step * 16, smem + ring + sdst[u]);
-  };
 
-  // ---- this wave's tiles --------------------------------------------------------------------------
-  // Activations come from the prologue's layouts, token-major inside each (step, piece): piece
-  // (s, r, g) of token t is 16 bytes at ((s * 16 + r) * Mp + t) * 16, with r = 4c + g for the bf16
-  // chunk c of the base product and r = 8 part + 4 half + g for the fp8 terms, so the 16 lanes of
-  // a lane group read 16 consecutive tokens (256 contiguous bytes).
-  // dense tiles (base sum): tokens 16*(wave + 8i) + j; lanes past the batch read zeros
-  const rsrc_t xrs = make_rsrc(xg);
-  const rsrc_t qrs = make_rsrc(qg);
-  const unsigned mp16 = (unsigned)a.Mp * 16;   // bytes between pieces of one token
+  // ---- activations: the prologue's layouts ------------------------------------------------------
+  // Piece (s, o, g) of token t is 16 bytes at (((s * 4 + o) * nblk + t / 16) * 4 + g) * 256 +
+  // (t % 16) * 16, nblk = Mp / 16: the 64 lanes of a 16-token aligned block read 1 KiB in lane
+  // order.  o = bf16 chunk c for the base operand, o = 2 part + half for the fp8 terms.
+  const rsrc_t xrs = make_rsrc(P.x);
+  const rsrc_t qrs = make_rsrc(P.xq);
+  const unsigned ostep = (unsigned)a.Mp * 64;   // bytes between consecutive o (= nblk KiB)
+  const int tb0 = a.tok_base >> 4;              // first 16-token block of this launch
   unsigned xoff[ND];
   bool dreal[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) {
     const int tile = wave + kWaves * i;
-    dreal[i] = 16 * tile < M;
-    const int t = 16 * tile + j;
-    xoff[i] = t < M ? (unsigned)g * mp16 + (unsigned)(a.tok0 + t) * 16 : kOob;
+    const int t = 16 * tile + j;                // relative to tok_base
+    dreal[i] = 16 * tile < hi_tok;
+    xoff[i] = (t >= lo_tok && t < hi_tok) ? (unsigned)(tb0 + tile) * 1024 + (unsigned)lane * 16
+                                          : kOob;
   }
-  // variant tiles (sign sum)
   unsigned qoff[NS];
   int sc_hi[NS], sc_lo[NS];
   unsigned tslot[NS];
@@ -244,13 +221,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
     const int ti_raw = wave * NS + i;
     const int ti = max(0, min(ti_raw, T - 1));  // T == 0: a batch of base-model tokens only
     const int valid = a.tile_valid[ti];
+    const int tr = max(lo_tok, min(a.tile_src[ti] + j, hi_tok - 1));  // relative token
+    const int t = a.tok_base + tr;
     // lanes past the tile's tokens read zeros without touching memory
-    const int tok = a.tok0 + max(0, min(a.tile_src[ti] + j, M - 1));
-    qoff[i] = (ti_raw < T && j < valid) ? (unsigned)g * mp16 + (unsigned)tok * 16 : kOob;
-    sc_hi[i] = P.xscale[tok];
+    qoff[i] = (ti_raw < T && j < valid)
+                  ? (unsigned)(t >> 4) * 1024 + (unsigned)g * 256 + (unsigned)(t & 15) * 16
+                  : kOob;
+    sc_hi[i] = P.xscale[t];
     sc_lo[i] = sc_hi[i] - 4;
     const int s = a.tile_slot[ti];
-    tslot[i] = __builtin_amdgcn_readfirstlane((unsigned)s * kSSlotG);
+    tslot[i] = __builtin_amdgcn_readfirstlane((unsigned)s * kSSlot);
     treal[i] = ti_raw < T;
     tnew[i] = i == 0 || a.tile_slot[max(0, min(ti_raw - 1, T - 1))] != s;
   }
@@ -268,83 +248,79 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) accd[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_xb = [&](int i, int s) {
-    const unsigned ks = (unsigned)min(s, nsteps - 1) * 16;
+  auto load_xb = [&](int i, unsigned s) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) xb[i][c] = load16(xrs, xoff[i] + (ks + 4 * c) * mp16);
+    for (int c = 0; c < 4; ++c) xb[i][c] = load16(xrs, xoff[i] + (s * 4 + c) * ostep);
   };
   // hi (part 0) or lo (part 1) fp8 term of variant tile i at step s: 32 bytes per lane
   auto load_xq_part = [&](int i, unsigned s, int part) {
-    const unsigned o = qoff[i] + (s * 16 + (unsigned)part * 8) * mp16;
+    const unsigned o = qoff[i] + (s * 4 + 2 * part) * ostep;
     const u32x4 v0 = load16(qrs, o);
-    const u32x4 v1 = load16(qrs, o + 4 * mp16);
+    const u32x4 v1 = load16(qrs, o + ostep);
     const i32x8 v = {(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
                      (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
     if (part == 0) xh[i] = v;
     else xl[i] = v;
   };
-  auto load_xq = [&](int i, int s) {
-    load_xq_part(i, (unsigned)min(s, nsteps - 1), 0);
-    load_xq_part(i, (unsigned)min(s, nsteps - 1), 1);
-  };
   // vector-memory instructions per step that are activation loads
   constexpr int kX = 4 * ND + 4 * NS;
 
-  // ---- prologue: stage 0 and 1 of W, sign group 0, activations of step 0 ------------------------
-  issue_w(0);
-  issue_signs(0);
+  // ---- prologue: stages 0..kAhead-1 and the activations of step 0 ------------------------------
 #pragma unroll
-  for (int s = 1; s < kWAhead; ++s) issue_w(s);
+  for (int s = 0; s < kAhead; ++s) issue(s);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < ND; ++i) load_xb(i, 0);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) load_xq(i, 0);
+  for (int i = 0; i < NS; ++i) {
+    load_xq_part(i, 0, 0);
+    load_xq_part(i, 0, 1);
+  }
   __builtin_amdgcn_sched_barrier(0);
   SPLIT_VMCNT(kX);
   raw_barrier();
 
   // per-lane LDS read offsets
   const unsigned a_lane = (unsigned)j * 256;                   // + stage + rt * 4096 + swizzled chunk
-  const unsigned s_lane = (unsigned)(j * 32 + 4 * g);          // + ring + slot + rt * 512 + step * 16
+  const unsigned s_lane = kWStage + (unsigned)(j * 16 + 4 * g);  // + stage + slot + rt * 256
 
   u32x4 S[kRT];
   for (int s = 0; s < nsteps; ++s) {
-    issue_w(s + kWAhead);
-    if ((s & 1) == 0) issue_signs((s >> 1) + 1);
+    issue(s + kAhead);
     __builtin_amdgcn_sched_barrier(0);
 
     // Each activation operand is reloaded for step s+1 right after its last use in step s, so
     // every load has about one step to arrive.
     const unsigned knext = (unsigned)min(s + 1, nsteps - 1);
+    const unsigned st = (unsigned)(s % kStages) * kStage;
 
     // base sum over the dense tiles, 32-column chunk by chunk
-    const unsigned wst = (unsigned)(s % kWStages) * kWStage + a_lane;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 A[kRT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
-        A[rt] = *reinterpret_cast<const u32x4*>(smem + wst + rt * 4096 + (((4 * c + g) ^ j) * 16));
+        A[rt] = *reinterpret_cast<const u32x4*>(smem + st + a_lane + rt * 4096 +
+                                                 (((4 * c + g) ^ j) * 16));
 #pragma unroll
       for (int i = 0; i < ND; ++i) {
         if (dreal[i]) {
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt) accb[i][rt] = mfma_bf16(A[rt], xb[i][c], accb[i][rt]);
         }
-        xb[i][c] = load16(xrs, xoff[i] + (knext * 16 + 4 * c) * mp16);
+        xb[i][c] = load16(xrs, xoff[i] + (knext * 4 + c) * ostep);
       }
     }
 
     // sign sum over this wave's variant tiles: hi terms, then lo terms
-    const unsigned sst = kSBase + (unsigned)((s >> 1) & 1) * kSGroup + (unsigned)(s & 1) * 16 + s_lane;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (treal[i]) {
         if (tnew[i]) {
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt)
-            S[rt] = expand_fp4(*reinterpret_cast<const unsigned*>(smem + sst + tslot[i] + rt * 512));
+            S[rt] = expand_fp4(
+                *reinterpret_cast<const unsigned*>(smem + st + s_lane + tslot[i] + rt * 256));
         }
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt)
@@ -359,13 +335,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
       load_xq_part(i, knext, 1);
     }
 
+    // Before the barrier, each wave waits for its copies of step s+1 (issued at least two steps
+    // ago, with at least 2 kX activation loads after them) but not for newer loads.
     __builtin_amdgcn_sched_barrier(0);
     SPLIT_VMCNT(2 * kX);
     raw_barrier();
   }
 
   // ---- epilogue ---------------------------------------------------------------------------------------
-  // alpha_v * sign sum -> E[token][row] (fp32, row stride kEStride); the W/sign rings are dead.
+  // alpha_v * sign sum -> E[token][row] (fp32, row stride kEStride); the LDS ring is dead.
   float* E = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -390,11 +368,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
   const bool vec_store = (d_out & 3) == 0;  // y rows start on 4-element boundaries
 #pragma unroll
   for (int i = 0; i < ND; ++i) {
-    const int t = 16 * (wave + kWaves * i) + j;
-    if (!dreal[i] || t >= M) continue;
-    const bool hd = (a.has_delta[t >> 5] >> (t & 31)) & 1u;
-    const float* e = E + t * kEStride + 4 * g;
-    const size_t ybase = (size_t)t * d_out;
+    const int tr = 16 * (wave + kWaves * i) + j;  // relative token
+    if (!dreal[i] || tr < lo_tok || tr >= hi_tok) continue;
+    const bool hd = (a.has_delta[tr >> 5] >> (tr & 31)) & 1u;
+    const float* e = E + tr * kEStride + 4 * g;
+    const size_t ybase = (size_t)(a.tok_base + tr) * d_out;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       const int orow = row0 + rt * 16 + 4 * g;
@@ -429,11 +407,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a) {
 // ---- activation prologue: x (bf16) -> the kernel's operand layouts ----------------------------
 // One workgroup per (token, linear).  Pass 1: the token's largest magnitude m; the fp8 scale is
 // 2^e with e = ceil(log2 m) - 8, so |x| * 2^-e <= 256 < 448 (the largest e4m3 value).  Pass 2:
-// one thread per 128-column step writes, token-major inside each 16-byte piece slot,
-//   * the bf16 activations in base-operand order: piece (s, 4c + g) = columns 128s+32c+8g..+7;
+// one thread per 128-column step writes, in 1 KiB blocks of 16 tokens (piece (s, o, g) of token
+// t at (((s * 4 + o) * Mp / 16 + t / 16) * 4 + g) * 256 + (t % 16) * 16),
+//   * the bf16 activations in base-operand order: piece (s, c, g) = columns 128s+32c+8g..+7;
 //   * hi = e4m3(v) and lo = e4m3(16 (v - hi)), v = x * 2^-e, each rounded to nearest even, in
-//     sign-operand order: piece (s, 8 part + 4 half + g) = bytes 16 half..16 half+15 of lane
-//     group g's 32 fp8 values (part 0 = hi, 1 = lo), positions mapped to columns as above.
+//     sign-operand order: piece (s, 2 part + half, g) = bytes 16 half..16 half+15 of lane group
+//     g's 32 fp8 values (part 0 = hi, 1 = lo), operand positions mapped to columns as above.
 constexpr int kActThreads = 128;
 
 __device__ __forceinline__ int col_of_position(int h) {  // operand position -> column, one step
@@ -445,9 +424,10 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
   const int t = blockIdx.x, p = blockIdx.y;
   const int d_in = a.d_in[p];
   const uint16_t* __restrict__ x = a.x[p] + (size_t)t * d_in;
-  const size_t mp16 = (size_t)a.Mp * 16;
-  unsigned char* __restrict__ xb = a.xb[p] + (size_t)t * 16;
-  unsigned char* __restrict__ q = a.xq[p] + (size_t)t * 16;
+  const size_t ostep = (size_t)a.Mp * 64;  // bytes between consecutive (s, o) block rows
+  const size_t tpos = (size_t)(t >> 4) * 1024 + (size_t)(t & 15) * 16;
+  unsigned char* __restrict__ xb = a.xb[p] + tpos;
+  unsigned char* __restrict__ q = a.xq[p] + tpos;
   const int tid = threadIdx.x;
 
   float m = 0.f;
@@ -485,8 +465,8 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
       v[4 * i + 1] = c[1];
       v[4 * i + 2] = c[2];
       v[4 * i + 3] = c[3];
-      // bf16 piece r = i (columns 8i..8i+7 = chunk i/4, group i%4)
-      *reinterpret_cast<u32x4*>(xb + ((size_t)s * 16 + i) * mp16) = c;
+      // bf16 piece (s, c = i / 4, g = i % 4): columns 8i..8i+7
+      *reinterpret_cast<u32x4*>(xb + ((size_t)s * 4 + (i >> 2)) * ostep + (size_t)(i & 3) * 256) = c;
     }
     unsigned hi[32], lo[32];
 #pragma unroll
@@ -516,9 +496,9 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int o = 8 * G + 4 * half;
-        *reinterpret_cast<u32x4*>(q + ((size_t)s * 16 + 4 * half + G) * mp16) =
+        *reinterpret_cast<u32x4*>(q + ((size_t)s * 4 + half) * ostep + (size_t)G * 256) =
             u32x4{hi[o], hi[o + 1], hi[o + 2], hi[o + 3]};
-        *reinterpret_cast<u32x4*>(q + ((size_t)s * 16 + 8 + 4 * half + G) * mp16) =
+        *reinterpret_cast<u32x4*>(q + ((size_t)s * 4 + 2 + half) * ostep + (size_t)G * 256) =
             u32x4{lo[o], lo[o + 1], lo[o + 2], lo[o + 3]};
       }
   }
@@ -553,7 +533,8 @@ hipError_t launch_split_act(const SplitActArgs& a, int M, int nprob, hipStream_t
 }
 
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
-  if (a.M < 1 || a.M > kSplitMaxM || a.ntiles < 0 || a.ntiles > kSplitMaxTiles ||
+  if (a.hi < 1 || a.hi > kSplitMaxM || a.lo < 0 || a.lo >= a.hi || (a.tok_base & 15) != 0 ||
+      a.ntiles < 0 || a.ntiles > kSplitMaxTiles ||
       a.nslots < 0 || a.nslots > kMaxSlots || a.nprob < 1 || a.nprob > kMaxProblems)
     return hipErrorInvalidValue;
   // grid: 8 XCD lists, each as long as the longest (see the block map in the kernel)
@@ -567,7 +548,7 @@ hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
     longest = len > longest ? len : longest;
   }
   const int nblocks = 8 * longest;
-  const int nd = (a.M + 16 * kWaves - 1) / (16 * kWaves);  // 1 or 2
+  const int nd = (a.hi + 16 * kWaves - 1) / (16 * kWaves);  // 1 or 2
   const int ns = a.ntiles == 0 ? 1 : (a.ntiles + kWaves - 1) / kWaves;  // 1..3
   if (nd == 1) {
     if (ns == 1) return launch_nd_ns<1, 1>(a, nblocks, stream);

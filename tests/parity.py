@@ -57,7 +57,8 @@ def oracle_delta_term(x, variants, seg_offsets, seg_variant, d_out, d_in):
 
 
 def gpu_compress(deltas_np, dev="cuda"):
-    """Compress every delta on the device; returns [(words_t, alpha_t)]."""
+    """Compress every delta on the device; returns [(words_t, alpha_t, tiled_t)] where tiled_t is
+    the tiled copy of the sign words (None when d_in is not a multiple of 128)."""
     import tenant_serving_bitdelta_amd as bd
     torch = torch_mod()
     out = []
@@ -65,6 +66,21 @@ def gpu_compress(deltas_np, dev="cuda"):
         dt = f32_dev(d, dev)
         words = torch.empty((d.shape[0], d.shape[1] // 32), dtype=torch.int32, device=dev)
         alpha = torch.empty(1, dtype=torch.float32, device=dev)
-        bd.compress(dt, words, alpha)
-        out.append((words, alpha))
+        nt = bd.sign_words_t128(d.shape[0], d.shape[1])
+        tiled = torch.empty(nt, dtype=torch.int32, device=dev) if nt > 0 else None
+        bd.compress(dt, words, alpha, tiled=tiled)
+        out.append((words, alpha, tiled))
+    return out
+
+
+def tile_words_128(words, d_out, d_in):
+    """Row-major sign words [d_out][d_in/32] -> the 128-row tiled order (padding rows zero): word
+    (r, c) goes to ((r // 128) * (d_in // 128) + c // 4) * 512 + (r % 128) * 4 + c % 4."""
+    wpr = d_in // 32
+    nrb = (d_out + 127) // 128
+    out = np.zeros(nrb * 128 * wpr, dtype=np.uint32)
+    r = np.arange(d_out)[:, None]
+    c = np.arange(wpr)[None, :]
+    idx = ((r // 128) * (d_in // 128) + c // 4) * 512 + (r % 128) * 4 + c % 4
+    out[idx.ravel()] = np.asarray(words, dtype=np.uint32).reshape(d_out, wpr).ravel()
     return out

@@ -37,13 +37,17 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.abi_version() == 2
+    assert bd.abi_version() == 3
     for s in range(7):
         assert L.bitdelta_status_string(s)
     assert L.bitdelta_status_string(99) == b"unknown status"
 
 
 def test_sign_words_and_workspace():
+    # tiled copy: rows padded to blocks of 128, same words per row
+    assert bd.sign_words_t128(4096, 4096) == 4096 * 128
+    assert bd.sign_words_t128(1000, 128) == 1024 * 4
+    assert bd.sign_words_t128(8, 96) == -1
     assert bd.sign_words(4096, 4096) == 4096 * 128
     assert bd.sign_words(256, 512) == 4096
     assert bd.sign_words(8, 33) == -1 and bd.sign_words(-1, 32) == -1
@@ -76,8 +80,8 @@ def test_plan_rejects_bad_ids():
         bd.plan_segments([0], 65)
 
 
-def _compress(delta, d_out, d_in, words, alpha, ws, ws_bytes):
-    return L.bitdelta_compress(delta, d_out, d_in, words, alpha, ws, ws_bytes, None)
+def _compress(delta, d_out, d_in, words, alpha, ws, ws_bytes, tiled=None):
+    return L.bitdelta_compress(delta, d_out, d_in, words, tiled, alpha, ws, ws_bytes, None)
 
 
 def test_compress_validation():
@@ -90,6 +94,10 @@ def test_compress_validation():
     assert _compress(FAKE, 64, 64, FAKE + 2, FAKE, FAKE, ws) == ALIGN
     assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE + 4, ws) == ALIGN
     assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE, ws - 8) == WORKSPACE
+    # the tiled copy needs d_in % 128 == 0 and 16-byte alignment
+    assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE, ws, tiled=FAKE) == SHAPE
+    ws2 = bd.compress_workspace_bytes(64, 128)
+    assert _compress(FAKE, 64, 128, FAKE, FAKE, FAKE, ws2, tiled=FAKE + 4) == ALIGN
 
 
 def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None, ws=FAKE,
@@ -99,8 +107,10 @@ def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None,
     op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     vp = v.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     varr = (bd._Variant * max(len(variants), 1))()
-    for i, (wd, al) in enumerate(variants):
-        varr[i].sign_words, varr[i].alpha = wd, al
+    for i, var in enumerate(variants):
+        varr[i].sign_words, varr[i].alpha = var[0], var[1]
+        if len(var) > 2:
+            varr[i].sign_words_t128 = var[2]
     if path is None:
         return L.bitdelta_matmul(x, w, m, d_out, d_in, varr, len(variants), op, vp, v.size, y,
                                  y_dtype, ws, ws_bytes, None)
@@ -143,6 +153,8 @@ def test_matmul_validation():
     # d_in = 64 is not a multiple of 128: the decode paths refuse it when forced
     assert call(path=2) == UNSUPPORTED
     assert call(path=4) == UNSUPPORTED
+    # SPLIT also needs the tiled sign words of every variant the batch uses
+    assert call(d_in=128, path=4) == UNSUPPORTED
     # an unused variant may be absent
     assert call(m=0, offs=[0, 0, 0]) == OK         # empty batch: nothing enqueued
     assert call(m=0, offs=[0], segv=[]) == OK
@@ -151,7 +163,7 @@ def test_matmul_validation():
 
 
 def test_split_workspace_validation():
-    V = [(FAKE, FAKE), (FAKE + 256, FAKE + 512)]
+    V = [(FAKE, FAKE, FAKE + 4096), (FAKE + 256, FAKE + 512, FAKE + 8192)]
     need = bd.matmul_workspace_bytes(8, 128)
     good = dict(x=FAKE, w=FAKE, m=8, d_out=64, d_in=128, variants=V, offs=[0, 3, 8], segv=[0, 1],
                 y=FAKE, path=4)

@@ -9,6 +9,7 @@ import pytest
 import oracle.bitdelta_oracle as O
 import workloads as WL
 from parity import (DELTA_RESIDUAL_TOL_BF16, ROW_L2_TOL, bf16_dev, delta_residual, f32_dev,
+                    tile_words_128,
                     gpu_compress, oracle_delta_term, row_rel_l2, words_host)
 
 pytestmark = pytest.mark.gpu
@@ -31,12 +32,19 @@ def _announce(request):
 # ----------------------------------------------------------------------------------------------
 
 def check_compress(delta):
-    (words, alpha), = gpu_compress([delta])
+    (words, alpha, tiled), = gpu_compress([delta])
     torch.cuda.synchronize()
     ref_words, ref_alpha = O.compress_ref(delta)
     np.testing.assert_array_equal(words_host(words), ref_words)
     a = float(alpha.cpu()[0])
     assert abs(a - float(ref_alpha)) <= 1e-6 * abs(float(ref_alpha)) or a == float(ref_alpha)
+    d_out, d_in = delta.shape
+    if tiled is not None:
+        # the tiled copy holds the same bits, chunk-reordered; padding rows are not written
+        want = tile_words_128(ref_words, d_out, d_in)
+        real = tile_words_128(np.ones_like(ref_words), d_out, d_in) == 1
+        got = tiled.cpu().numpy().view(np.uint32)
+        np.testing.assert_array_equal(got[real], want[real])
     return words, alpha
 
 
@@ -71,7 +79,7 @@ def test_compress_all_zero_and_repeatable():
     assert float(alpha.cpu()[0]) == 0.0 and np.all(words_host(words) == 0xFFFFFFFF)
     rng = np.random.default_rng(11)
     d = rng.laplace(0, 2e-4, size=(300, 2048)).astype(np.float32)
-    (w1, a1), (w2, a2) = gpu_compress([d, d])
+    (w1, a1, _), (w2, a2, _) = gpu_compress([d, d])
     torch.cuda.synchronize()
     assert torch.equal(w1, w2) and torch.equal(a1, a2)
 
@@ -168,13 +176,13 @@ def test_identity_readback_exact():
     w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
     delta = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
     x_bits = WL.f32_to_bf16_bits(np.eye(d_in, dtype=np.float32))
-    (words, alpha), = gpu_compress([delta])
+    (words, alpha, tiled), = gpu_compress([delta])
     ref_words, ref_alpha = O.compress_ref(delta)
     weff = O.reconstruct_ref(O.bf16_bits_to_f64(w_bits), ref_words, ref_alpha)  # fp64 exact
     want_f32 = weff.astype(np.float32).T
     want_bf16 = O.bf16_bits_to_f64(WL.f32_to_bf16_bits(weff.astype(np.float32))).T
     for path in ("stream", "split", "prefill"):
-        y = bd.matmul(bf16_dev(x_bits), bf16_dev(w_bits), [(words, alpha)], [0, d_in], [0],
+        y = bd.matmul(bf16_dev(x_bits), bf16_dev(w_bits), [(words, alpha, tiled)], [0, d_in], [0],
                       out_dtype="f32", path=path)
         got = y.cpu().numpy()
         want = want_bf16 if path == "prefill" else want_f32
@@ -186,7 +194,7 @@ def test_gemv_readback_exact():
     d_out, d_in = 40, 96
     w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
     delta = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
-    (words, alpha), = gpu_compress([delta])
+    (words, alpha, tiled), = gpu_compress([delta])
     ref_words, ref_alpha = O.compress_ref(delta)
     weff = O.reconstruct_ref(O.bf16_bits_to_f64(w_bits), ref_words, ref_alpha).astype(np.float32)
     for k in (0, 31, 32, 95):
