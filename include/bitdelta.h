@@ -95,6 +95,11 @@ int bitdelta_abi_version(void);
 /* Static string naming a status code. */
 const char* bitdelta_status_string(int status);
 
+/* The hipError_t code behind the most recent BITDELTA_ERR_HIP returned on the calling thread
+ * (0 if there was none), and the HIP runtime's static string for it. */
+int32_t bitdelta_last_hip_error(void);
+const char* bitdelta_last_hip_error_string(void);
+
 /* Number of uint32 sign words of a d_out x d_in matrix (d_out * d_in / 32), or -1 if d_in is
  * not a positive multiple of 32 or d_out is negative. */
 int64_t bitdelta_sign_words(int64_t d_out, int64_t d_in);

@@ -31,6 +31,8 @@ class BitDeltaError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = int(status)
         name = _lib().bitdelta_status_string(int(status)).decode() if _LIB is not None else str(status)
+        if self.status == 6 and _LIB is not None:  # BITDELTA_ERR_HIP: name the runtime's error
+            name += f" [{_LIB.bitdelta_last_hip_error_string().decode()}]"
         super().__init__(f"{what}: {name} (status {status})" if what else f"{name} (status {status})")
 
 
@@ -57,10 +59,16 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+        # torch first: its HIP runtime is then the one the library binds to.  Loaded the other
+        # way round, a process can end up with two HIP runtimes (torch's bundled copy and the
+        # system one) whose kernels and device memory do not mix.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.bitdelta_abi_version.restype = ctypes.c_int
         L.bitdelta_status_string.restype = ctypes.c_char_p
         L.bitdelta_status_string.argtypes = [ctypes.c_int]
+        L.bitdelta_last_hip_error.restype = ctypes.c_int32
+        L.bitdelta_last_hip_error_string.restype = ctypes.c_char_p
         L.bitdelta_sign_words.restype = ctypes.c_int64
         L.bitdelta_sign_words.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.bitdelta_compress_workspace_bytes.restype = ctypes.c_size_t

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <utility>
 #include <vector>
 
@@ -15,7 +16,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
-bitdelta_status map_hip(hipError_t e) { return e == hipSuccess ? BITDELTA_OK : BITDELTA_ERR_HIP; }
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+bitdelta_status map_hip(hipError_t e) {
+  if (e == hipSuccess) return BITDELTA_OK;
+  g_last_hip_error = e;
+  return BITDELTA_ERR_HIP;
+}
 
 struct Segment {
   int begin, len, variant;
@@ -212,115 +219,195 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
   return BITDELTA_OK;
 }
 
-// ---- split-activation decode: chunks of <= 256 tokens, <= 24 variant tiles, <= 16 variants ---
+// ---- split-activation decode ----------------------------------------------------------------
+// A launch covers the tokens [t_begin, t_end) of at most 16 aligned 16-token blocks (dense
+// tiles) and at most 16 variants.  The distinct variants of a tile's tokens form (tile, variant)
+// pairs.  Tiles go to the 8 waves of a workgroup, at most nd per wave, each to the wave with the
+// least work so far (a dense tile costs about as much as two pairs), such that no wave holds more
+// than kSplitMaxPairs pairs.  A launch ends before the first run of same-variant tokens
+// that would break a limit.
+struct SplitPlan {
+  int t_begin = 0, t_end = 0, tok_base = 0, nd = 1, npw = 0;
+  std::vector<int> slot_var;
+  bd::SplitWave wv[8];
+  int8_t token_slot[bd::kSplitMaxM];
+};
+
+bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* pl) {
+  const int tok_base = t_begin / 16 * 16;
+  const int ntiles = (t_end - 1 - tok_base) / 16 + 1;
+  if (ntiles > bd::kSplitMaxM / 16) return false;
+  std::vector<int> slot_var;
+  int8_t token_slot[bd::kSplitMaxM];
+  memset(token_slot, -1, sizeof(token_slot));
+  for (int t = t_begin; t < t_end; ++t) {
+    if (tv[t] < 0) continue;
+    int slot = -1;
+    for (int q = 0; q < (int)slot_var.size(); ++q)
+      if (slot_var[q] == tv[t]) slot = q;
+    if (slot < 0) {
+      if ((int)slot_var.size() == bd::kMaxSlots) return false;
+      slot_var.push_back(tv[t]);
+      slot = (int)slot_var.size() - 1;
+    }
+    token_slot[t - tok_base] = (int8_t)slot;
+  }
+  const int nd = ntiles <= 8 ? 1 : 2;
+  const int maxp = bd::kSplitMaxPairs;
+  // the distinct slots of each tile, ascending
+  std::vector<std::vector<int>> tslots(ntiles);
+  for (int i = 0; i < ntiles; ++i) {
+    unsigned seen = 0;
+    for (int t = 16 * i; t < 16 * i + 16; ++t)
+      if (token_slot[t] >= 0) seen |= 1u << token_slot[t];
+    for (int q = 0; q < bd::kMaxSlots; ++q)
+      if (seen >> q & 1u) tslots[i].push_back(q);
+    if ((int)tslots[i].size() > maxp) return false;
+  }
+  std::vector<int> order(ntiles);
+  for (int i = 0; i < ntiles; ++i) order[i] = i;
+  for (int i = 1; i < ntiles; ++i)  // stable, most pairs first
+    for (int k = i; k > 0 && tslots[order[k]].size() > tslots[order[k - 1]].size(); --k)
+      std::swap(order[k], order[k - 1]);
+  int wt[8] = {0}, wp[8] = {0};
+  std::vector<int> owner(ntiles, -1), slot_in_wave(ntiles, 0);
+  for (int i : order) {
+    const int np_i = (int)tslots[i].size();
+    int best = -1;
+    for (int w = 0; w < 8; ++w) {
+      if (wt[w] >= nd || wp[w] + np_i > maxp) continue;
+      // waves w and w + 4 share a SIMD: break ties by the SIMD's work
+      const int cost = 2 * wt[w] + wp[w], simd = cost + 2 * wt[w ^ 4] + wp[w ^ 4];
+      if (best < 0) { best = w; continue; }
+      const int bcost = 2 * wt[best] + wp[best], bsimd = bcost + 2 * wt[best ^ 4] + wp[best ^ 4];
+      if (cost < bcost || (cost == bcost && simd < bsimd)) best = w;
+    }
+    if (best < 0) return false;
+    owner[i] = best;
+    slot_in_wave[i] = wt[best]++;
+    wp[best] += np_i;
+  }
+  pl->t_begin = t_begin;
+  pl->t_end = t_end;
+  pl->tok_base = tok_base;
+  pl->nd = nd;
+  pl->slot_var = slot_var;
+  memcpy(pl->token_slot, token_slot, sizeof(token_slot));
+  pl->npw = 0;
+  for (int w = 0; w < 8; ++w) {
+    bd::SplitWave& W = pl->wv[w];
+    W.tile[0] = W.tile[1] = -1;
+    for (int q = 0; q < bd::kSplitMaxPairs; ++q) {
+      W.pair_tile[q] = -1;
+      W.pair_slot[q] = 0;
+    }
+    std::vector<std::pair<int, int>> pairs;  // (slot, tile of the wave), by slot so that pairs
+    for (int i = 0; i < ntiles; ++i) {       // of one variant reuse the expanded signs
+      if (owner[i] != w) continue;
+      W.tile[slot_in_wave[i]] = i;
+      for (int q : tslots[i]) pairs.push_back({q, slot_in_wave[i]});
+    }
+    std::sort(pairs.begin(), pairs.end());
+    for (int k = 0; k < (int)pairs.size(); ++k) {
+      W.pair_slot[k] = pairs[k].first;
+      W.pair_tile[k] = pairs[k].second;
+    }
+    pl->npw = std::max(pl->npw, (int)pairs.size());
+  }
+  return true;
+}
+
 bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
                           const std::vector<Segment>& segs, int y_f32, void* workspace,
                           hipStream_t st) {
-  // workspace: per problem, fp8 hi/lo activations then the per-token scale codes
-  bd::SplitActArgs act;
-  memset(&act, 0, sizeof(act));
+  // workspace, per problem: bf16 pieces, fp6 pieces, block scales
   const int Mp = (int)((M + 15) / 16 * 16);
-  act.Mp = Mp;
-  std::vector<unsigned char*> xb(np), xq(np);
-  std::vector<int*> xs(np);
+  std::vector<unsigned char*> xb(np), xq(np), xs(np);
   size_t off = 0;
   for (int p = 0; p < np; ++p) {
     unsigned char* base = static_cast<unsigned char*>(workspace) + off;
-    const size_t qbytes = ((size_t)Mp * 2 * (size_t)probs[p].d_in + 255) / 256 * 256;
+    size_t bb, qb, cb;
+    bd::split_workspace_parts(M, probs[p].d_in, &bb, &qb, &cb);
     xb[p] = base;
-    xq[p] = base + qbytes;
-    xs[p] = reinterpret_cast<int*>(base + 2 * qbytes);
-    off += bd::split_workspace_bytes(M, probs[p].d_in);
-    act.x[p] = static_cast<const uint16_t*>(probs[p].x);
-    act.xb[p] = xb[p];
-    act.xq[p] = xq[p];
-    act.xscale[p] = xs[p];
-    act.d_in[p] = (int)probs[p].d_in;
+    xq[p] = base + bb;
+    xs[p] = base + bb + qb;
+    off += bb + qb + cb;
   }
-  bitdelta_status r = map_hip(bd::launch_split_act(act, (int)M, np, st));
-  if (r != BITDELTA_OK) return r;
-
   // problems with longer rows first, so the longest workgroups do not form the tail
   std::vector<int> order(np);
   for (int p = 0; p < np; ++p) order[p] = p;
-  for (int i = 1; i < np; ++i)
-    for (int k = i; k > 0 && probs[order[k]].d_in > probs[order[k - 1]].d_in; --k)
-      std::swap(order[k], order[k - 1]);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int l, int r) { return probs[l].d_in > probs[r].d_in; });
 
-  struct Unit {
-    int tok, n, variant;
-  };
-  std::vector<Unit> units;
+  std::vector<int> tv((size_t)M, -1);
   for (const Segment& s : segs)
-    for (int r0 = 0; r0 < s.len; r0 += 16) units.push_back({s.begin + r0, s.len - r0 < 16 ? s.len - r0 : 16, s.variant});
-  size_t u0 = 0;
-  while (u0 < units.size()) {
-    const int t_begin = units[u0].tok;
-    const int tok_base = t_begin / 16 * 16;   // launches cover whole 16-token blocks
-    std::vector<int> slot_var;
-    int ntiles = 0;
-    size_t u1 = u0;
-    while (u1 < units.size()) {
-      const Unit& u = units[u1];
-      if (u.tok + u.n - tok_base > bd::kSplitMaxM) break;
-      if (u.variant >= 0) {
-        if (ntiles == bd::kSplitMaxTiles) break;
-        bool have = false;
-        for (int v : slot_var) have = have || v == u.variant;
-        if (!have && (int)slot_var.size() == bd::kMaxSlots) break;
-        if (!have) slot_var.push_back(u.variant);
-        ++ntiles;
-      }
-      ++u1;
+    for (int t = s.begin; t < s.begin + s.len; ++t) tv[t] = s.variant;
+
+  int t_begin = 0;
+  while (t_begin < M) {
+    // grow the launch one run (same variant, same 16-token block) at a time
+    SplitPlan plan;
+    const int limit = (int)std::min<int64_t>(M, t_begin / 16 * 16 + bd::kSplitMaxM);
+    int t = t_begin;
+    while (t < limit) {
+      int e = t + 1;
+      while (e < limit && e % 16 != 0 && tv[e] == tv[t]) ++e;
+      SplitPlan cand;
+      if (!plan_split(tv, t_begin, e, &cand)) break;
+      plan = cand;
+      t = e;
     }
-    const int t_end = units[u1 - 1].tok + units[u1 - 1].n;
+    // one run fits any launch (one tile, at most one pair, one variant)
+    if (plan.t_end <= t_begin) return BITDELTA_ERR_UNSUPPORTED;
+
     bd::SplitArgs a;
     memset(&a, 0, sizeof(a));
-    a.tok_base = tok_base;
-    a.lo = t_begin - tok_base;
-    a.hi = t_end - tok_base;
+    a.tok_base = plan.tok_base;
+    a.lo = plan.t_begin - plan.tok_base;
+    a.hi = plan.t_end - plan.tok_base;
     a.Mp = Mp;
-    a.ntiles = ntiles;
-    a.nslots = (int)slot_var.size();
+    a.nslots = (int)plan.slot_var.size();
     a.y_f32 = y_f32;
-    int ti = 0;
-    for (size_t i = u0; i < u1; ++i) {
-      const Unit& u = units[i];
-      if (u.variant < 0) continue;
-      int slot = 0;
-      for (int q = 0; q < (int)slot_var.size(); ++q)
-        if (slot_var[q] == u.variant) slot = q;
-      a.tile_slot[ti] = (int8_t)slot;
-      a.tile_valid[ti] = (uint8_t)u.n;
-      a.tile_src[ti] = (int16_t)(u.tok - tok_base);
-      ++ti;
-      for (int t = u.tok - tok_base; t < u.tok - tok_base + u.n; ++t)
-        a.has_delta[t >> 5] |= 1u << (t & 31);
-    }
+    memcpy(a.wv, plan.wv, sizeof(a.wv));
+    memcpy(a.token_slot, plan.token_slot, sizeof(a.token_slot));
+    bd::SplitActArgs act;
+    memset(&act, 0, sizeof(act));
+    act.Mp = Mp;
+    act.tok_base = a.tok_base;
+    act.lo = a.lo;
+    memcpy(act.token_slot, plan.token_slot, sizeof(act.token_slot));
     for (int p0 = 0; p0 < np; p0 += bd::kMaxProblems) {
-      const int pn = np - p0 < bd::kMaxProblems ? np - p0 : bd::kMaxProblems;
+      const int pn = std::min(np - p0, bd::kMaxProblems);
       a.nprob = pn;
+      act.nprob = pn;
       for (int q = 0; q < pn; ++q) {
         const int p = order[p0 + q];
         const bitdelta_problem& P = probs[p];
+        act.x[q] = static_cast<const uint16_t*>(P.x);
+        act.xb[q] = xb[p];
+        act.xq[q] = xq[p];
+        act.xs[q] = xs[p];
+        act.d_in[q] = (int)P.d_in;
         bd::SplitProblem& S = a.prob[q];
         S.x = xb[p];
         S.xq = xq[p];
-        S.xscale = xs[p];
+        S.xs = xs[p];
         S.w = static_cast<const uint16_t*>(P.w_base);
         S.y = P.y;
         S.d_out = (int)P.d_out;
         S.d_in = (int)P.d_in;
         S.nblocks = (int)((P.d_out + bd::kSplitRows - 1) / bd::kSplitRows);
-        for (int s = 0; s < (int)slot_var.size(); ++s) {
-          S.words[s] = P.variants[slot_var[s]].sign_words_t128;
-          S.alpha[s] = P.variants[slot_var[s]].alpha;
+        for (int s = 0; s < (int)plan.slot_var.size(); ++s) {
+          S.words[s] = P.variants[plan.slot_var[s]].sign_words_t128;
+          act.alpha[q][s] = P.variants[plan.slot_var[s]].alpha;
         }
       }
-      r = map_hip(bd::launch_split(a, st));
+      bitdelta_status r = map_hip(bd::launch_split_act(act, plan.t_end - plan.t_begin, st));
+      if (r != BITDELTA_OK) return r;
+      r = map_hip(bd::launch_split(a, plan.nd, plan.npw, st));
       if (r != BITDELTA_OK) return r;
     }
-    u0 = u1;
+    t_begin = plan.t_end;
   }
   return BITDELTA_OK;
 }
@@ -398,6 +485,10 @@ const char* bitdelta_status_string(int status) {
     default: return "unknown status";
   }
 }
+
+int32_t bitdelta_last_hip_error(void) { return (int32_t)g_last_hip_error; }
+
+const char* bitdelta_last_hip_error_string(void) { return hipGetErrorString(g_last_hip_error); }
 
 int64_t bitdelta_sign_words(int64_t d_out, int64_t d_in) {
   if (d_out < 0 || d_in <= 0 || d_in % 32 != 0 || d_out >= kMaxDim || d_in >= kMaxDim) return -1;

@@ -25,6 +25,11 @@ __device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Launch status: hipGetLastError() also returns an error left behind by an earlier runtime call
+// of the same thread (another library's query, say), so each launcher clears it first and the
+// check after the launch reports that launch alone.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 // ---------------------------------------------------------------------------------------------
 // Compress (two passes)
 // ---------------------------------------------------------------------------------------------
@@ -99,48 +104,62 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Decode with the sign product on fp4 x fp8 MFMA (activations split into two exact fp8 terms
-// by a prologue kernel into caller workspace).  Needs d_in % 128 == 0 and 16-byte aligned sign
-// words.  One launch serves a token range of at most kSplitMaxM tokens (16 dense tiles) with at
-// most kSplitMaxTiles 16-token variant tiles and kMaxSlots distinct variants.
+// Decode with the sign product on fp4 x fp6 MFMA.  A prologue kernel writes, per launch chunk,
+// the bf16 activations and the variant-scaled activations x' = alpha_v * x as two fp6 (e2m3)
+// terms with per-32-column block scales, in operand layouts, into caller workspace.  Needs
+// d_in % 128 == 0 and the tiled sign words.  One launch serves the tokens of at most 16 aligned
+// 16-token blocks and at most kMaxSlots distinct variants, with at most kSplitMaxPairs
+// (block, variant) pairs per wave.
 constexpr int kSplitMaxM = 256;
-constexpr int kSplitMaxTiles = 24;
-constexpr int kSplitRows = 64;
+constexpr int kSplitRows = 128;
+constexpr int kSplitMaxPairs = 8;
 
 struct SplitProblem {
   const unsigned char* x;     // bf16 activations in base-operand order (prologue layout)
-  const unsigned char* xq;    // fp8 hi/lo in sign-operand order (prologue layout)
-  const int* xscale;          // [Mp] E8M0 code of the hi term (lo: code - 4)
+  const unsigned char* xq;    // fp6 hi/lo terms of alpha * x in sign-operand order
+  const unsigned char* xs;    // E8M0 block scales of the two terms
   const uint16_t* w;
   void* y;                    // [M][d_out] of the whole call
   int d_out, d_in;
-  int nblocks, pad_;          // 64-row blocks of this linear
+  int nblocks, pad_;          // 128-row blocks of this linear
   const uint32_t* words[kMaxSlots];  // tiled sign words (128-row layout)
-  const float* alpha[kMaxSlots];
+};
+
+// Per-wave work of a split launch.  32-bit fields: the kernel reads them with scalar loads
+// indexed by the wave, whose addresses must stay 4-byte aligned.
+struct SplitWave {
+  int32_t tile[2];                       // 16-token block (relative) of the dense tiles, -1 none
+  int32_t pair_tile[kSplitMaxPairs];     // which of the two tiles a pair belongs to, -1 none
+  int32_t pair_slot[kSplitMaxPairs];     // the pair's variant slot
 };
 
 struct SplitArgs {
   SplitProblem prob[kMaxProblems];
-  int nprob, ntiles, nslots, y_f32;
+  int nprob, nslots, y_f32;
   int tok_base;                          // first token of this launch's 16-token blocks
   int lo, hi;                            // tokens [tok_base + lo, tok_base + hi) are this launch's
-  int Mp;                                // token count of the layouts (call's M rounded up to 16)
-  uint32_t has_delta[kSplitMaxM / 32];  // bit t: token tok_base + t belongs to a variant
-  int8_t tile_slot[kSplitMaxTiles];     // slot of the tile's variant
-  uint8_t tile_valid[kSplitMaxTiles];   // real tokens in the tile (1..16)
-  int16_t tile_src[kSplitMaxTiles];     // first token of the tile, relative to tok_base
+  int Mp, pad_;                          // token count of the layouts (call's M rounded up to 16)
+  SplitWave wv[8];
+  int8_t token_slot[kSplitMaxM];         // slot of token tok_base + t (-1 = base model); read per lane
 };
-hipError_t launch_split(const SplitArgs& a, hipStream_t stream);  // grid from nblocks
+// nd: dense tiles per wave (1 or 2); npw: pairs per wave (at most kSplitMaxPairs).
+hipError_t launch_split(const SplitArgs& a, int nd, int npw, hipStream_t stream);
 
 struct SplitActArgs {
   const uint16_t* x[kMaxProblems];     // bf16 [M][d_in] row-major (the caller's activations)
   unsigned char* xb[kMaxProblems];     // out: bf16 in base-operand order
-  unsigned char* xq[kMaxProblems];     // out: fp8 hi/lo in sign-operand order
-  int* xscale[kMaxProblems];           // out: [M] scale codes
+  unsigned char* xq[kMaxProblems];     // out: fp6 hi/lo terms of alpha * x in sign-operand order
+  unsigned char* xs[kMaxProblems];     // out: their block scales
+  const float* alpha[kMaxProblems][kMaxSlots];
   int d_in[kMaxProblems];
-  int Mp, pad_;                        // token stride of the layouts (M rounded up to 16)
+  int Mp, tok_base, lo, nprob;         // tokens tok_base + lo + blockIdx.x
+  int8_t token_slot[kSplitMaxM];       // slot of token tok_base + t (-1 = base model)
 };
-hipError_t launch_split_act(const SplitActArgs& a, int M, int nprob, hipStream_t stream);
-size_t split_workspace_bytes(int64_t M, int64_t d_in);  // per linear, multiple of 256
+// ntok tokens from tok_base + lo, for a.nprob linears
+hipError_t launch_split_act(const SplitActArgs& a, int ntok, hipStream_t stream);
+// Workspace of one linear: bf16 pieces, fp6 pieces, scales; each part a multiple of 256 bytes.
+size_t split_workspace_bytes(int64_t M, int64_t d_in);
+void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq_bytes,
+                           size_t* xs_bytes);
 
 }  // namespace bd

@@ -132,6 +132,7 @@ int compress_grid(int64_t n) {
 hipError_t launch_compress(const float* delta, int64_t n, int64_t d_in, uint32_t* words,
                            uint32_t* tiled, float* alpha, double* partials, hipStream_t stream) {
   const int grid = compress_grid(n);
+  clear_stale_error();
   hipLaunchKernelGGL(compress_pass1, dim3(grid), dim3(kThreads), 0, stream,
                      reinterpret_cast<const f32x4*>(delta), n / 4, words, tiled, d_in / 32,
                      partials);

@@ -127,6 +127,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   const int rows_per_block = kRows * (kThreads / 64);
   const dim3 grid((a.d_out + rows_per_block - 1) / rows_per_block);
+  clear_stale_error();
   switch (a.M) {
     case 1: hipLaunchKernelGGL(gemv_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
     case 2: hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;

@@ -199,6 +199,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   }
   const size_t lds = (size_t)2 * (kPrefillBM + kPrefillBN) * kStride * 2;
   const int nblocks = a.n_mtiles * a.n_ntiles;
+  clear_stale_error();
   hipLaunchKernelGGL(prefill_kernel, dim3(nblocks), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }

@@ -297,6 +297,7 @@ hipError_t launch_ntw(const StreamArgs& a, int nblocks, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
+  clear_stale_error();
   hipLaunchKernelGGL(stream_kernel<NTW>, dim3(nblocks), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }

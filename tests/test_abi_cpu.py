@@ -181,10 +181,11 @@ def test_split_workspace_validation():
 
 
 def test_matmul_workspace_bytes():
-    # per token (M rounded up to 16): a bf16 copy and the fp8 hi + lo terms (2 bytes per element
-    # each) plus one int32 scale code, each region rounded up to 256 bytes
-    assert bd.matmul_workspace_bytes(256, 8192) == 2 * 256 * 2 * 8192 + 1024
-    assert bd.matmul_workspace_bytes(5, 128, "split") == 2 * 16 * 256 + 256
+    # per token (M rounded up to 16): a bf16 copy (2 bytes per element), the two fp6 terms
+    # (1.5 bytes per element) and one 4-byte scale word per 32 elements, each region rounded
+    # up to 256 bytes
+    assert bd.matmul_workspace_bytes(256, 8192) == 256 * 8192 * 2 + 256 * 8192 * 3 // 2 + 256 * 8192 // 8
+    assert bd.matmul_workspace_bytes(5, 128, "split") == 16 * 128 * 2 + 16 * 128 * 3 // 2 + 256
     assert bd.matmul_workspace_bytes(4, 8192) == 0            # AUTO -> GEMV, no workspace
     assert bd.matmul_workspace_bytes(300, 8192) == 0          # AUTO -> PREFILL
     assert bd.matmul_workspace_bytes(64, 8192, "stream") == 0
