@@ -222,16 +222,22 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
 // ---- split-activation decode ----------------------------------------------------------------
 // A launch covers the tokens [t_begin, t_end) of at most 16 aligned 16-token blocks (dense
 // tiles) and at most 16 variants.  The distinct variants of a tile's tokens form (tile, variant)
-// pairs.  Tiles go to the 8 waves of a workgroup, at most nd per wave, each to the wave with the
-// least work so far (a dense tile costs about as much as two pairs), such that no wave holds more
-// than kSplitMaxPairs pairs.  A launch ends before the first run of same-variant tokens
-// that would break a limit.
+// pairs.  Neighbouring tiles are handed out together (2 per wave when there are more than 8
+// tiles), because tokens arrive grouped by variant and the pairs of one variant in both tiles of
+// a wave share one expansion of the sign words; a wave's pairs are arranged as slot groups, one
+// variant per group.  Tile units go to the waves longest first, each to the SIMD (waves w and
+// w + 4) with the least estimated work.  A launch ends before the first run of same-variant
+// tokens that would give a wave more than kSplitMaxGroups groups.
 struct SplitPlan {
-  int t_begin = 0, t_end = 0, tok_base = 0, nd = 1, npw = 0;
+  int t_begin = 0, t_end = 0, tok_base = 0, nd = 1, ng = 0;
   std::vector<int> slot_var;
   bd::SplitWave wv[8];
   int8_t token_slot[bd::kSplitMaxM];
 };
+
+// Estimated SIMD cycles per K step: the base product of one dense tile (32 bf16 MFMAs), one
+// pair (16 fp4 x fp6 MFMAs and the lane masking) and one expansion of a variant's sign words.
+constexpr int kCostTile = 512, kCostPair = 320, kCostExpand = 224;
 
 bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* pl) {
   const int tok_base = t_begin / 16 * 16;
@@ -253,39 +259,42 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
     token_slot[t - tok_base] = (int8_t)slot;
   }
   const int nd = ntiles <= 8 ? 1 : 2;
-  const int maxp = bd::kSplitMaxPairs;
-  // the distinct slots of each tile, ascending
-  std::vector<std::vector<int>> tslots(ntiles);
-  for (int i = 0; i < ntiles; ++i) {
-    unsigned seen = 0;
+  // the distinct slots of each tile, as a bit set
+  std::vector<unsigned> tset(ntiles, 0u);
+  for (int i = 0; i < ntiles; ++i)
     for (int t = 16 * i; t < 16 * i + 16; ++t)
-      if (token_slot[t] >= 0) seen |= 1u << token_slot[t];
-    for (int q = 0; q < bd::kMaxSlots; ++q)
-      if (seen >> q & 1u) tslots[i].push_back(q);
-    if ((int)tslots[i].size() > maxp) return false;
+      if (token_slot[t] >= 0) tset[i] |= 1u << token_slot[t];
+  // units: single tiles, or neighbouring pairs of tiles
+  struct Unit {
+    int tile[2];
+    int ngroups, cost;
+  };
+  std::vector<Unit> units;
+  for (int i = 0; i < ntiles; i += nd) {
+    Unit u;
+    u.tile[0] = i;
+    u.tile[1] = (nd == 2 && i + 1 < ntiles) ? i + 1 : -1;
+    const unsigned s0 = tset[i], s1 = u.tile[1] >= 0 ? tset[i + 1] : 0u;
+    const int n0 = __builtin_popcount(s0), n1 = __builtin_popcount(s1);
+    const int shared = __builtin_popcount(s0 & s1);
+    u.ngroups = shared + std::max(n0 - shared, n1 - shared);
+    u.cost = kCostTile * (u.tile[1] >= 0 ? 2 : 1) + kCostPair * (n0 + n1) +
+             kCostExpand * __builtin_popcount(s0 | s1);
+    if (u.ngroups > bd::kSplitMaxGroups) return false;
+    units.push_back(u);
   }
-  std::vector<int> order(ntiles);
-  for (int i = 0; i < ntiles; ++i) order[i] = i;
-  for (int i = 1; i < ntiles; ++i)  // stable, most pairs first
-    for (int k = i; k > 0 && tslots[order[k]].size() > tslots[order[k - 1]].size(); --k)
-      std::swap(order[k], order[k - 1]);
-  int wt[8] = {0}, wp[8] = {0};
-  std::vector<int> owner(ntiles, -1), slot_in_wave(ntiles, 0);
-  for (int i : order) {
-    const int np_i = (int)tslots[i].size();
+  std::vector<int> order(units.size());
+  for (size_t k = 0; k < units.size(); ++k) order[k] = (int)k;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int l, int r) { return units[l].cost > units[r].cost; });
+  int simd_load[4] = {0, 0, 0, 0}, simd_waves[4] = {0, 0, 0, 0};
+  std::vector<int> wave_of(units.size(), -1);
+  for (int k : order) {
     int best = -1;
-    for (int w = 0; w < 8; ++w) {
-      if (wt[w] >= nd || wp[w] + np_i > maxp) continue;
-      // waves w and w + 4 share a SIMD: break ties by the SIMD's work
-      const int cost = 2 * wt[w] + wp[w], simd = cost + 2 * wt[w ^ 4] + wp[w ^ 4];
-      if (best < 0) { best = w; continue; }
-      const int bcost = 2 * wt[best] + wp[best], bsimd = bcost + 2 * wt[best ^ 4] + wp[best ^ 4];
-      if (cost < bcost || (cost == bcost && simd < bsimd)) best = w;
-    }
-    if (best < 0) return false;
-    owner[i] = best;
-    slot_in_wave[i] = wt[best]++;
-    wp[best] += np_i;
+    for (int sm = 0; sm < 4; ++sm)
+      if (simd_waves[sm] < 2 && (best < 0 || simd_load[sm] < simd_load[best])) best = sm;
+    wave_of[k] = best + 4 * simd_waves[best]++;
+    simd_load[best] += units[k].cost;
   }
   pl->t_begin = t_begin;
   pl->t_end = t_end;
@@ -293,26 +302,30 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
   pl->nd = nd;
   pl->slot_var = slot_var;
   memcpy(pl->token_slot, token_slot, sizeof(token_slot));
-  pl->npw = 0;
+  pl->ng = 0;
   for (int w = 0; w < 8; ++w) {
     bd::SplitWave& W = pl->wv[w];
     W.tile[0] = W.tile[1] = -1;
-    for (int q = 0; q < bd::kSplitMaxPairs; ++q) {
-      W.pair_tile[q] = -1;
-      W.pair_slot[q] = 0;
+    for (int q = 0; q < bd::kSplitMaxGroups; ++q) W.slot[q][0] = W.slot[q][1] = -1;
+  }
+  for (size_t k = 0; k < units.size(); ++k) {
+    bd::SplitWave& W = pl->wv[wave_of[k]];
+    const Unit& u = units[k];
+    W.tile[0] = u.tile[0];
+    W.tile[1] = u.tile[1];
+    const unsigned s0 = tset[u.tile[0]], s1 = u.tile[1] >= 0 ? tset[u.tile[1]] : 0u;
+    int g = 0;
+    for (int q = 0; q < bd::kMaxSlots; ++q)  // variants of both tiles: one group each
+      if ((s0 & s1) >> q & 1u) {
+        W.slot[g][0] = W.slot[g][1] = q;
+        ++g;
+      }
+    int g0 = g, g1 = g;  // the others side by side
+    for (int q = 0; q < bd::kMaxSlots; ++q) {
+      if ((s0 & ~s1) >> q & 1u) W.slot[g0++][0] = q;
+      if ((s1 & ~s0) >> q & 1u) W.slot[g1++][1] = q;
     }
-    std::vector<std::pair<int, int>> pairs;  // (slot, tile of the wave), by slot so that pairs
-    for (int i = 0; i < ntiles; ++i) {       // of one variant reuse the expanded signs
-      if (owner[i] != w) continue;
-      W.tile[slot_in_wave[i]] = i;
-      for (int q : tslots[i]) pairs.push_back({q, slot_in_wave[i]});
-    }
-    std::sort(pairs.begin(), pairs.end());
-    for (int k = 0; k < (int)pairs.size(); ++k) {
-      W.pair_slot[k] = pairs[k].first;
-      W.pair_tile[k] = pairs[k].second;
-    }
-    pl->npw = std::max(pl->npw, (int)pairs.size());
+    pl->ng = std::max(pl->ng, std::max(g0, g1));
   }
   return true;
 }
@@ -404,7 +417,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
       }
       bitdelta_status r = map_hip(bd::launch_split_act(act, plan.t_end - plan.t_begin, st));
       if (r != BITDELTA_OK) return r;
-      r = map_hip(bd::launch_split(a, plan.nd, plan.npw, st));
+      r = map_hip(bd::launch_split(a, plan.nd, plan.ng, st));
       if (r != BITDELTA_OK) return r;
     }
     t_begin = plan.t_end;

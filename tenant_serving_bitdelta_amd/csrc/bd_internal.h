@@ -108,11 +108,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // the bf16 activations and the variant-scaled activations x' = alpha_v * x as two fp6 (e2m3)
 // terms with per-32-column block scales, in operand layouts, into caller workspace.  Needs
 // d_in % 128 == 0 and the tiled sign words.  One launch serves the tokens of at most 16 aligned
-// 16-token blocks and at most kMaxSlots distinct variants, with at most kSplitMaxPairs
-// (block, variant) pairs per wave.
+// 16-token blocks and at most kMaxSlots distinct variants, with at most kSplitMaxGroups slot
+// groups per wave.
 constexpr int kSplitMaxM = 256;
 constexpr int kSplitRows = 128;
-constexpr int kSplitMaxPairs = 8;
+constexpr int kSplitMaxGroups = 8;
 
 struct SplitProblem {
   const unsigned char* x;     // bf16 activations in base-operand order (prologue layout)
@@ -129,8 +129,7 @@ struct SplitProblem {
 // indexed by the wave, whose addresses must stay 4-byte aligned.
 struct SplitWave {
   int32_t tile[2];                       // 16-token block (relative) of the dense tiles, -1 none
-  int32_t pair_tile[kSplitMaxPairs];     // which of the two tiles a pair belongs to, -1 none
-  int32_t pair_slot[kSplitMaxPairs];     // the pair's variant slot
+  int32_t slot[kSplitMaxGroups][2];      // slot group g: the variant slot of tile i's pair, -1 none
 };
 
 struct SplitArgs {
@@ -142,8 +141,8 @@ struct SplitArgs {
   SplitWave wv[8];
   int8_t token_slot[kSplitMaxM];         // slot of token tok_base + t (-1 = base model); read per lane
 };
-// nd: dense tiles per wave (1 or 2); npw: pairs per wave (at most kSplitMaxPairs).
-hipError_t launch_split(const SplitArgs& a, int nd, int npw, hipStream_t stream);
+// nd: dense tiles per wave (1 or 2); ng: slot groups per wave (at most kSplitMaxGroups).
+hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream);
 
 struct SplitActArgs {
   const uint16_t* x[kMaxProblems];     // bf16 [M][d_in] row-major (the caller's activations)

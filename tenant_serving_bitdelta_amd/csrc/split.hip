@@ -32,8 +32,9 @@
 // operands agree on every product.  The block scale of lane group G covers columns 32G..32G+31.
 //
 // Work split.  A workgroup (8 waves, two per SIMD) owns 128 output rows of one linear and up to
-// 256 tokens (16 dense tiles).  The host gives each wave up to ND dense tiles and up to NPW
-// (tile, variant) pairs of its own tiles, balancing the matrix-core work of the waves.  The K
+// 256 tokens (16 dense tiles).  The host gives each wave up to ND dense tiles (neighbouring
+// ones, which share variants) and their (tile, variant) pairs, as NG slot groups of one variant
+// each, balancing the work of the SIMDs.  The K
 // loop walks d_in in steps of 128:
 //   * W_base (128 rows x 128, 32 KiB) and the sign words of every active variant (the tiled
 //     copy: 128 rows x 16 B = 2 KiB contiguous per variant and step) are copied by direct
@@ -60,6 +61,7 @@ constexpr int kKS = 128;                 // k per step
 constexpr unsigned kWStage = kRows * kKS * 2;        // 32 KiB of W_base per step
 constexpr unsigned kSSlot = kRows * 16;              // one variant's sign words, one step: 2 KiB
 constexpr unsigned kLdsCap = 160 * 1024;             // LDS of one compute unit
+constexpr int kCopyWaves = 4;                        // waves that issue the global->LDS copies
 static_assert(kWStage + kMaxSlots * kSSlot <= kLdsCap / 2, "two stages must fit in LDS");
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -129,7 +131,7 @@ __device__ __forceinline__ void raw_barrier() {
 template <int N>
 constexpr int cmin63() { return N > 63 ? 63 : N; }
 
-template <int ND, int NPW>
+template <int ND, int NG>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, unsigned stage_bytes,
                                                             int nst) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -167,38 +169,36 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   const int j = lane & 15, g = lane >> 4;
 
   // ---- direct copies (global -> LDS), `ahead` steps ahead, into stage s % nst ------------------
-  // W_base: copy b = 4*wave + u (of 32) moves rows 4b..4b+3 of the block for one step, 256 bytes
+  // Waves 0-3 (one per SIMD) issue every copy, 16 each per step, spread over their sign phase,
+  // so that the other wave of each SIMD is never held up by a full memory-instruction queue.
+  // W_base: copy b = 8*wave + u (of 32) moves rows 4b..4b+3 of the block for one step, 256 bytes
   // each, so every 4 consecutive lanes read 64 contiguous bytes.  Lane L writes LDS slot
   // (row 4b + L/16, 16-byte position L%16) and fetches 16-byte column chunk position ^ (row%16):
   // the XOR swizzle keeps the MFMA operand reads below conflict-free.
+  const bool copier = wave < kCopyWaves;
+  const int cw = copier ? wave : 0;
   const rsrc_t wrs = make_rsrc(P.w + (size_t)row0 * d_in);
-  unsigned woff[4];
+  unsigned woff[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int rl = 4 * (4 * wave + u) + (lane >> 4);
+  for (int u = 0; u < 8; ++u) {
+    const int rl = 4 * (8 * cw + u) + (lane >> 4);
     const int row = min(row0 + rl, d_out - 1) - row0;
     woff[u] = (unsigned)((row * d_in + 8 * ((lane & 15) ^ (rl & 15))) * 2);
   }
   // sign words (tiled layout): the 128 rows of this block for one step are 2 KiB contiguous at
-  // word (rb * nsteps + s) * 512.  Copy q = wave + 8u moves half q % 2 of slot q / 2.
-  rsrc_t srs[4];
-  bool sreal[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = wave + kWaves * u;
-    sreal[u] = q < 2 * nslots;
-    srs[u] = make_rsrc(P.words[sreal[u] ? q >> 1 : 0]);
-  }
-  const unsigned soff = (unsigned)rb * (unsigned)nsteps * 2048u + (unsigned)(wave & 1) * 1024u +
+  // word (rb * nsteps + s) * 512.  Copy q = wave + 4u moves half q % 2 of slot q / 2.
+  const unsigned soff = (unsigned)rb * (unsigned)nsteps * 2048u + (unsigned)(cw & 1) * 1024u +
                         (unsigned)lane * 16u;
-  auto issue = [&](int s, unsigned st) {  // copies for step s into the stage at byte st
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      dma16(wrs, woff[u] + (unsigned)s * (kKS * 2), smem + st + (4 * wave + u) * 1024);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (sreal[u])
-        dma16(srs[u], soff + (unsigned)s * 2048u, smem + st + kWStage + (wave + kWaves * u) * 1024);
+  // copy k (< 16) of this wave for step s into the stage at byte st
+  auto copy = [&](int k, int s, unsigned st) {
+    if (k < 8) {
+      dma16(wrs, woff[k] + (unsigned)s * (kKS * 2), smem + st + (8 * cw + k) * 1024);
+    } else {
+      const int q = cw + kCopyWaves * (k - 8);
+      if (q < 2 * nslots)
+        dma16(make_rsrc(P.words[q >> 1]), soff + (unsigned)s * 2048u,
+              smem + st + kWStage + q * 1024);
+    }
   };
 
   // ---- activations: the prologue's layouts ------------------------------------------------------
@@ -227,20 +227,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     qoff[i] = tq ? (unsigned)(tb0 + tile) * 1024 + (unsigned)lane * 16 : kOob;
     coff[i] = tq ? (unsigned)(tb0 + tile) * 256 + (unsigned)lane * 4 : kOob;
   }
-  int ptile[NPW];
-  unsigned pslot[NPW];
-  bool pnew[NPW], pin[NPW];
+  // slot groups: group q holds the pair (dense tile i, variant slot gslot[q][i]) of each tile i
+  // that has one (slot -1: none); pin marks the lanes whose token belongs to that variant
+  int gslot[NG][ND];
+  bool pin[NG][ND];
 #pragma unroll
-  for (int q = 0; q < NPW; ++q) {
-    const int pt = a.wv[wave].pair_tile[q];
-    const int slot = a.wv[wave].pair_slot[q];
-    ptile[q] = pt;
-    pslot[q] = (unsigned)max(slot, 0) * kSSlot;
-    pnew[q] = q == 0 || a.wv[wave].pair_slot[q - 1] != slot || a.wv[wave].pair_tile[q - 1] < 0;
-    const int tile = pt >= 0 ? a.wv[wave].tile[pt] : -1;
-    const int t = 16 * tile + j;
-    pin[q] = tile >= 0 && t >= lo_tok && t < hi_tok && a.token_slot[t] == slot;
-  }
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int slot = a.wv[wave].slot[q][i];
+      gslot[q][i] = slot;
+      const int t = 16 * a.wv[wave].tile[i] + j;
+      pin[q][i] = slot >= 0 && dreal[i] && t >= lo_tok && t < hi_tok && a.token_slot[t] == slot;
+    }
 
   // ---- registers ------------------------------------------------------------------------------------
   u32x4 xb[ND][4];           // bf16 activations of the dense tiles, 4 chunks of 32 columns
@@ -265,7 +264,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   constexpr int kX = 8 * ND;
 
   // ---- prologue: stages 0..ahead-1 and the activations of step 0 -------------------------------
-  for (int s = 0; s < ahead && s < nsteps; ++s) issue(s, (unsigned)s * stage_bytes);
+  if (copier)
+    for (int s = 0; s < ahead && s < nsteps; ++s)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) copy(k, s, (unsigned)s * stage_bytes);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < ND; ++i) load_xq(i, 0);
@@ -282,48 +284,53 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   unsigned st = 0;                                     // stage of step s
   unsigned st_next = (unsigned)ahead * stage_bytes;    // stage of step s + ahead
   const unsigned ring = (unsigned)nst * stage_bytes;
+  // sign sum over this wave's slot groups, into the dense tiles.  The fp4 operands of a group's
+  // variant are expanded once for both of its tiles; each pair issues its 8 hi-term MFMAs before
+  // its 8 lo-term MFMAs, so dependent MFMAs are 8 apart.  With copies, the wave issues 16 / NG of
+  // its copies of step cs before each group.
   u32x4 S[kRT];
-  for (int s = 0; s < nsteps; ++s) {
-    if (s + ahead < nsteps) issue(s + ahead, st_next);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Each activation operand is reloaded for step s+1 right after its last use in step s, so
-    // every load has about one step to arrive.
-    const unsigned knext = (unsigned)min(s + 1, nsteps - 1);
-
-    // sign sum over this wave's pairs, into the pair's dense tile: hi terms, then lo terms
+  auto pair_mfma = [&](int i, bool in) {
+    const i32x8 bh = {in ? (int)xq[i][0][0] : 0, in ? (int)xq[i][0][1] : 0,
+                      in ? (int)xq[i][0][2] : 0, in ? (int)xq[i][0][3] : 0,
+                      in ? (int)xq[i][1][0] : 0, in ? (int)xq[i][1][1] : 0, 0, 0};
 #pragma unroll
-    for (int q = 0; q < NPW; ++q) {
-      const int pt = ptile[q];
-      if (pt >= 0 && pnew[q]) {
+    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, (int)xs[i], acc[i][rt]);
+    const i32x8 bl = {in ? (int)xq[i][1][2] : 0, in ? (int)xq[i][1][3] : 0,
+                      in ? (int)xq[i][2][0] : 0, in ? (int)xq[i][2][1] : 0,
+                      in ? (int)xq[i][2][2] : 0, in ? (int)xq[i][2][3] : 0, 0, 0};
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
-          S[rt] = expand_fp4(
-              *reinterpret_cast<const unsigned*>(smem + st + s_lane + pslot[q] + rt * 256));
+    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<1>(S[rt], bl, (int)xs[i], acc[i][rt]);
+  };
+  auto expand = [&](int slot, unsigned st) {
+    const unsigned char* sw = smem + st + s_lane + (unsigned)slot * kSSlot;
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+      S[rt] = expand_fp4(*reinterpret_cast<const unsigned*>(sw + rt * 256));
+  };
+  auto sign_phase = [&](bool copies, int cs, unsigned cst, unsigned st) {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      if (copies) {
+#pragma unroll
+        for (int k = q * (16 / NG); k < (q + 1) * (16 / NG); ++k) copy(k, cs, cst);
       }
-#pragma unroll
-      for (int i = 0; i < ND; ++i) {
-        if (pt == i) {
-          const bool in = pin[q];
-          const i32x8 bh = {in ? (int)xq[i][0][0] : 0, in ? (int)xq[i][0][1] : 0,
-                            in ? (int)xq[i][0][2] : 0, in ? (int)xq[i][0][3] : 0,
-                            in ? (int)xq[i][1][0] : 0, in ? (int)xq[i][1][1] : 0, 0, 0};
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            acc[i][rt] = mfma_sign<0>(S[rt], bh, (int)xs[i], acc[i][rt]);
-          const i32x8 bl = {in ? (int)xq[i][1][2] : 0, in ? (int)xq[i][1][3] : 0,
-                            in ? (int)xq[i][2][0] : 0, in ? (int)xq[i][2][1] : 0,
-                            in ? (int)xq[i][2][2] : 0, in ? (int)xq[i][2][3] : 0, 0, 0};
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            acc[i][rt] = mfma_sign<1>(S[rt], bl, (int)xs[i], acc[i][rt]);
+      const int s0 = gslot[q][0];
+      if (s0 >= 0) {
+        expand(s0, st);
+        pair_mfma(0, pin[q][0]);
+      }
+      if (ND == 2) {
+        const int s1 = gslot[q][ND - 1];
+        if (s1 >= 0) {
+          if (s1 != s0) expand(s1, st);
+          pair_mfma(ND - 1, pin[q][ND - 1]);
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < ND; ++i) load_xq(i, knext);
-
-    // base sum over the dense tiles, 32-column chunk by chunk
+  };
+  // base sum over the dense tiles, 32-column chunk by chunk, reloading each bf16 chunk for
+  // step kn right after its use
+  auto base_phase = [&](unsigned kn, unsigned st) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 A[kRT];
@@ -337,14 +344,24 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_bf16(A[rt], xb[i][c], acc[i][rt]);
         }
-        xb[i][c] = load16(xrs, xoff[i] + (knext * 4 + c) * ostep);
+        xb[i][c] = load16(xrs, xoff[i] + (kn * 4 + c) * ostep);
       }
     }
+  };
+
+  for (int s = 0; s < nsteps; ++s) {
+    // Each activation operand is reloaded for step s+1 right after its last use in step s, so
+    // every load has most of a step to arrive.
+    const unsigned knext = (unsigned)min(s + 1, nsteps - 1);
+    sign_phase(copier && s + ahead < nsteps, s + ahead, st_next, st);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) load_xq(i, knext);
+    base_phase(knext, st);
 
     // Before the barrier, each wave waits for its copies of step s+1 but not for newer loads:
-    // after those copies it issued `ahead` steps of activation loads (kX each) and at most
-    // ahead - 1 steps of copies (<= 8 each, no more than kX), and the activation loads of the
-    // older steps have completed (their values were used).
+    // after those copies it issued `ahead` steps of activation loads (kX each) and ahead - 1
+    // steps of copies, and the activation loads of the older steps have completed (their values
+    // were used).  Waves without copies wait for nothing that is still needed.
     __builtin_amdgcn_sched_barrier(0);
     if (ahead == 1) SPLIT_VMCNT(cmin63<kX>());
     else if (ahead == 2) SPLIT_VMCNT(cmin63<2 * kX>());
@@ -519,18 +536,18 @@ int lds_limit() {
   return cached[dev];
 }
 
-template <int ND, int NPW>
-hipError_t launch_nd_npw(const SplitArgs& a, int nblocks, unsigned stage, int nst,
+template <int ND, int NG>
+hipError_t launch_nd_ng(const SplitArgs& a, int nblocks, unsigned stage, int nst,
                          hipStream_t stream) {
   static bool configured = false;  // benign race: every caller sets the same value
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<ND, NPW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<ND, NG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_limit());
     if (e != hipSuccess) return e;
     configured = true;
   }
   clear_stale_error();
-  hipLaunchKernelGGL((split_kernel<ND, NPW>), dim3(nblocks), dim3(kThreads), nst * stage, stream,
+  hipLaunchKernelGGL((split_kernel<ND, NG>), dim3(nblocks), dim3(kThreads), nst * stage, stream,
                      a, stage, nst);
   return hipGetLastError();
 }
@@ -562,21 +579,21 @@ hipError_t launch_split_act(const SplitActArgs& a, int ntok, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_split(const SplitArgs& a, int nd, int npw, hipStream_t stream) {
+hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) {
   if (a.hi < 1 || a.hi > kSplitMaxM || a.lo < 0 || a.lo >= a.hi || (a.tok_base & 15) != 0 ||
       a.nslots < 0 || a.nslots > kMaxSlots || a.nprob < 1 || a.nprob > kMaxProblems ||
-      nd < 1 || nd > 2 || npw < 0 || npw > kSplitMaxPairs)
+      nd < 1 || nd > 2 || ng < 0 || ng > kSplitMaxGroups)
     return hipErrorInvalidValue;
   for (int w = 0; w < kWaves; ++w) {
     const SplitWave& W = a.wv[w];
     for (int i = 0; i < 2; ++i)
       if (W.tile[i] >= kSplitMaxM / 16 || (i >= nd && W.tile[i] >= 0)) return hipErrorInvalidValue;
-    for (int q = 0; q < kSplitMaxPairs; ++q) {
-      const int pt = W.pair_tile[q];
-      if (pt >= nd || (q >= npw && pt >= 0)) return hipErrorInvalidValue;
-      if (pt >= 0 && (W.tile[pt] < 0 || W.pair_slot[q] < 0 || W.pair_slot[q] >= a.nslots))
-        return hipErrorInvalidValue;
-    }
+    for (int q = 0; q < kSplitMaxGroups; ++q)
+      for (int i = 0; i < 2; ++i) {
+        const int slot = W.slot[q][i];
+        if (slot < -1 || slot >= a.nslots) return hipErrorInvalidValue;
+        if (slot >= 0 && (q >= ng || i >= nd || W.tile[i] < 0)) return hipErrorInvalidValue;
+      }
   }
   const int lds = lds_limit();
   const unsigned stage = kWStage + (unsigned)a.nslots * kSSlot;
@@ -595,13 +612,15 @@ hipError_t launch_split(const SplitArgs& a, int nd, int npw, hipStream_t stream)
   }
   const int nblocks = 8 * longest;
   if (nd == 1) {
-    if (npw <= 2) return launch_nd_npw<1, 2>(a, nblocks, stage, nst, stream);
-    if (npw <= 4) return launch_nd_npw<1, 4>(a, nblocks, stage, nst, stream);
-    return launch_nd_npw<1, 8>(a, nblocks, stage, nst, stream);
+    if (ng <= 1) return launch_nd_ng<1, 1>(a, nblocks, stage, nst, stream);
+    if (ng <= 2) return launch_nd_ng<1, 2>(a, nblocks, stage, nst, stream);
+    if (ng <= 4) return launch_nd_ng<1, 4>(a, nblocks, stage, nst, stream);
+    return launch_nd_ng<1, 8>(a, nblocks, stage, nst, stream);
   }
-  if (npw <= 2) return launch_nd_npw<2, 2>(a, nblocks, stage, nst, stream);
-  if (npw <= 4) return launch_nd_npw<2, 4>(a, nblocks, stage, nst, stream);
-  return launch_nd_npw<2, 8>(a, nblocks, stage, nst, stream);
+  if (ng <= 1) return launch_nd_ng<2, 1>(a, nblocks, stage, nst, stream);
+  if (ng <= 2) return launch_nd_ng<2, 2>(a, nblocks, stage, nst, stream);
+  if (ng <= 4) return launch_nd_ng<2, 4>(a, nblocks, stage, nst, stream);
+  return launch_nd_ng<2, 8>(a, nblocks, stage, nst, stream);
 }
 
 }  // namespace bd
