@@ -45,7 +45,55 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--path", default="auto", choices=("auto", "gemv", "stream", "split", "prefill"),
                    help="decode kernel family (auto: what the library picks)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only copy a 1 GiB device buffer three times (a plain copy kernel of known "
+                        "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+# ---------------------------------------------------------------------------------------------
+# measured HBM traffic of the split kernel (rocprofv3 counters, summarised under profiles/)
+# ---------------------------------------------------------------------------------------------
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "split_kernel__decode_20x70b_m256_14var__hbm_traffic.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "tenant_serving_bitdelta_amd", "csrc", f)
+                   for f in ("split.hip", "bd_internal.h", "api.cpp")]
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when the split-path
+    sources changed since the counters were taken (or there is no summary)."""
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    sha = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not val or sha.group(1) != sources_sha256():
+        return None
+    return int(val.group(1))
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 3}}
 
 
 # ---------------------------------------------------------------------------------------------
@@ -223,7 +271,7 @@ def run_decode(args, torch, bd, config):
 
     cpu = None
     if not args.no_cpu_baseline:
-        sample = [l for l in linears if l[0] in ("q", "k", "v", "o")] or linears
+        sample = [l for l in linears if l[0] in ("q", "k", "v", "o", "gate")] or linears
         cpu = cpu_baseline_decode(torch, config, sample, scales, perm, offs, segv, m, total_elems,
                                   nvar)
 
@@ -245,7 +293,8 @@ def run_decode(args, torch, bd, config):
                    "parallelism": "single GPU"},
         "hbm_gbs_step": bytes_launch * len(layers) / (ms_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if (config == 5 and path == 4) else None,
                      "kernel": {1: "gemv_kernel", 2: "stream_kernel",
                                 4: "split_act_kernel + split_kernel"}.get(path, "?"),
                      "bytes_per_launch": bytes_launch, "avg_launch_us": avg_launch_s * 1e6},
@@ -322,6 +371,9 @@ def main():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(torch)), flush=True)
+        return
     if args.config == 4:
         res = run_prefill(args, torch, bd)
     else:

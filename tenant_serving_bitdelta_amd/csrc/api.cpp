@@ -388,6 +388,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
     act.Mp = Mp;
     act.tok_base = a.tok_base;
     act.lo = a.lo;
+    act.hi = a.hi;
     memcpy(act.token_slot, plan.token_slot, sizeof(act.token_slot));
     for (int p0 = 0; p0 < np; p0 += bd::kMaxProblems) {
       const int pn = std::min(np - p0, bd::kMaxProblems);
@@ -415,7 +416,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
           act.alpha[q][s] = P.variants[plan.slot_var[s]].alpha;
         }
       }
-      bitdelta_status r = map_hip(bd::launch_split_act(act, plan.t_end - plan.t_begin, st));
+      bitdelta_status r = map_hip(bd::launch_split_act(act, st));
       if (r != BITDELTA_OK) return r;
       r = map_hip(bd::launch_split(a, plan.nd, plan.ng, st));
       if (r != BITDELTA_OK) return r;

@@ -151,11 +151,10 @@ struct SplitActArgs {
   unsigned char* xs[kMaxProblems];     // out: their block scales
   const float* alpha[kMaxProblems][kMaxSlots];
   int d_in[kMaxProblems];
-  int Mp, tok_base, lo, nprob;         // tokens tok_base + lo + blockIdx.x
-  int8_t token_slot[kSplitMaxM];       // slot of token tok_base + t (-1 = base model)
+  int Mp, tok_base, lo, hi, nprob, pad_;  // tokens [tok_base + lo, tok_base + hi)
+  int8_t token_slot[kSplitMaxM];       // slot of token tok_base + t (-1 = base model); read per lane
 };
-// ntok tokens from tok_base + lo, for a.nprob linears
-hipError_t launch_split_act(const SplitActArgs& a, int ntok, hipStream_t stream);
+hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream);
 // Workspace of one linear: bf16 pieces, fp6 pieces, scales; each part a multiple of 256 bytes.
 size_t split_workspace_bytes(int64_t M, int64_t d_in);
 void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq_bytes,

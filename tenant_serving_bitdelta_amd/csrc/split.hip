@@ -411,33 +411,37 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 }
 
 // ---- activation prologue: x (bf16) -> the kernel's operand layouts ----------------------------
-// One workgroup per (token, linear); one thread per 128-column step writes the token's pieces
-// (layouts above).  Every token gets its bf16 pieces; a token of variant v also gets the two
-// fp6 terms of x' = alpha_v * x with their block scales.
-constexpr int kActThreads = 128;
+// A workgroup covers one 16-token block and 4 K steps of one linear, one wave per step; lane
+// L = 16 g + j writes token j's 16-byte slot of every 1 KiB piece of that step (layouts above), so
+// each piece is written whole by one wave.  Every token gets its bf16 pieces; a token of variant
+// v also gets the two fp6 terms of x' = alpha_v * x for its 32-column block g, with their block
+// scales.  Lanes of tokens outside the launch write nothing.
+constexpr int kActThreads = 256;
+constexpr int kActSteps = kActThreads / 64;
 
 // Exponent a with m <= 7.5 * 2^a < 2 m (m > 0, finite): the block scale that puts m in the top
-// binade of e2m3.  m = f 2^E with f in [0.5, 1), and 7.5 = 0.9375 * 2^3.
+// binade of e2m3.  m = 1.f * 2^E, and 7.5 = 1.875 * 2^2: a = E - 2 for 1.f <= 1.875, else E - 1.
 __device__ __forceinline__ int e2m3_block_exp(float m) {
-  int E;
-  const float f = frexpf(m, &E);
-  return f <= 0.9375f ? E - 3 : E - 2;
+  const unsigned b = __float_as_uint(m);
+  if ((b >> 23) == 0u) {  // subnormal m
+    int E;
+    const float f = frexpf(m, &E);  // m = f 2^E, f in [0.5, 1)
+    return f <= 0.9375f ? E - 3 : E - 2;
+  }
+  const int E = (int)(b >> 23) - 127;
+  return (b & 0x7FFFFFu) <= 0x700000u ? E - 2 : E - 1;
 }
 
-// e2m3 code of v (|v| <= 7.5) rounded to nearest even, and the value of that code.  The grid
-// spacing is 2^(e - 3) in [2^e, 2^(e+1)) for e >= 0 and 1/8 below 1 (subnormals).
+// e2m3 code of v (|v| <= 7.5) rounded to nearest even, and the value of that code.  In the
+// binade [2^e, 2^(e+1)), e = 0, 1, 2, the grid spacing is 2^(e-3) (and 1/8 below 1, the
+// subnormals): the nearest grid point is n 2^(e-3) with n = rint(|v| 2^(3-e)) in [0, 16], and
+// its code is n + 8e (n = 16 is the first point of the next binade, whose code is 8 (e+1) + 8).
 __device__ __forceinline__ unsigned e2m3_round(float v, float* value) {
   const float a = fabsf(v);
-  int e = 0;
-  if (a >= 1.f) {
-    (void)frexpf(a, &e);
-    e -= 1;                                  // a in [2^e, 2^(e+1))
-  }
-  const float q = __uint_as_float((unsigned)(127 + e - 3) << 23);  // 2^(e-3), exact
-  const float r = rintf(a / q) * q;          // a / q is exact (power-of-two divisor)
-  // code: 8r below 2 (subnormals and [1, 2)), 8 + 4r in [2, 4), 16 + 2r in [4, 7.5]
-  const unsigned c = r < 2.f ? (unsigned)(8.f * r) : r < 4.f ? (unsigned)(8.f + 4.f * r)
-                                                              : (unsigned)(16.f + 2.f * r);
+  const int e = max((int)(__float_as_uint(a) >> 23) - 127, 0);
+  const float n = rintf(a * __uint_as_float((unsigned)(130 - e) << 23));  // exact scaling
+  const float r = n * __uint_as_float((unsigned)(124 + e) << 23);
+  const unsigned c = (unsigned)n + 8u * (unsigned)e;
   *value = v < 0.f ? -r : r;
   return (v < 0.f && r != 0.f) ? (c | 32u) : c;
 }
@@ -453,73 +457,74 @@ __device__ __forceinline__ void put6(unsigned* w, int f, unsigned c) {
   if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
 }
 
-__global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActArgs a) {
-  const int tr = a.lo + (int)blockIdx.x;     // token relative to tok_base
-  const int t = a.tok_base + tr, p = blockIdx.y;
+__global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActArgs a, int nsq) {
+  const int p = blockIdx.y;
+  const int d_in = a.d_in[p], nsteps = d_in / 128;
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int s = (int)(blockIdx.x % nsq) * kActSteps + (int)(threadIdx.x >> 6);
+  if (s >= nsteps) return;                   // wave-uniform
+  const int tb = (a.tok_base + a.lo) / 16 + (int)(blockIdx.x / nsq);  // absolute 16-token block
+  const int t = 16 * tb + j, tr = t - a.tok_base;
+  if (tr < a.lo || tr >= a.hi) return;       // not a token of this launch
   const int slot = a.token_slot[tr];
-  const int d_in = a.d_in[p];
-  const uint16_t* __restrict__ x = a.x[p] + (size_t)t * d_in;
   const size_t nblk = (size_t)a.Mp / 16;
   const size_t ostep = nblk * 1024;          // bytes between consecutive pieces
-  const size_t tpos = (size_t)(t >> 4) * 1024 + (size_t)(t & 15) * 16;
-  unsigned char* __restrict__ xb = a.xb[p] + tpos;
-  unsigned char* __restrict__ xq = a.xq[p] + tpos;
-  unsigned char* __restrict__ xs = a.xs[p] + (size_t)(t >> 4) * 256 + (size_t)(t & 15) * 4;
-  const int nsteps = d_in / 128;
-  const float alpha = slot >= 0 ? *a.alpha[p][slot] : 0.f;
+  const size_t pbase = (size_t)tb * 1024 + (size_t)lane * 16;
+  const uint16_t* __restrict__ x = a.x[p] + (size_t)t * d_in + (size_t)s * 128;
 
-  for (int s = threadIdx.x; s < nsteps; s += kActThreads) {
-    unsigned v[64];  // bf16 pairs of columns 128 s .. 128 s + 127
+  // bf16 pieces (s, c): columns 32c + 8g .. +7 of the step
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x4 c = *reinterpret_cast<const u32x4*>(x + (size_t)s * 128 + 8 * i);
-      v[4 * i] = c[0];
-      v[4 * i + 1] = c[1];
-      v[4 * i + 2] = c[2];
-      v[4 * i + 3] = c[3];
-      // bf16 piece (s, c = i / 4), lane group g = i % 4: columns 8i..8i+7
-      *reinterpret_cast<u32x4*>(xb + ((size_t)s * 4 + (i >> 2)) * ostep + (size_t)(i & 3) * 256) = c;
-    }
-    if (slot < 0) continue;  // base-model token: no sign term
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<u32x4*>(a.xb[p] + ((size_t)s * 4 + c) * ostep + pbase) =
+        *reinterpret_cast<const u32x4*>(x + 32 * c + 8 * g);
+  if (slot < 0) return;  // base-model token: no sign term
+
+  // fp6 terms of block g: columns 32g .. 32g+31 of the step
+  const float alpha = *a.alpha[p][slot];
+  unsigned v[16];
 #pragma unroll
-    for (int G = 0; G < 4; ++G) {  // block G: columns 32G..32G+31 of the step, lane group G
-      float xp[32];                // x' in operand order: field f <- column 32G + 4 (f % 8) + f / 8
-      float m = 0.f;
-#pragma unroll
-      for (int f = 0; f < 32; ++f) {
-        const int col = 32 * G + 4 * (f & 7) + (f >> 3);
-        const unsigned pair = v[col >> 1];
-        xp[f] = alpha * ((col & 1) ? bf16hi_to_f32(pair) : bf16lo_to_f32(pair));
-        m = fmaxf(m, fabsf(xp[f]));
-      }
-      int ea = m > 0.f ? e2m3_block_exp(m) : 0;
-      ea = max(-126, min(127, ea));
-      const float sa = pow2f(ea), inva = pow2f(-min(ea, 126));
-      unsigned hi[6] = {0, 0, 0, 0, 0, 0}, lo[6] = {0, 0, 0, 0, 0, 0};
-      float rm = 0.f;
-#pragma unroll
-      for (int f = 0; f < 32; ++f) {
-        float hv;
-        put6(hi, f, e2m3_round(xp[f] * inva, &hv));
-        xp[f] -= hv * sa;                    // remainder
-        rm = fmaxf(rm, fabsf(xp[f]));
-      }
-      int eb = rm > 0.f ? e2m3_block_exp(rm) : ea;
-      eb = max(-126, min(127, eb));
-      const float invb = pow2f(-min(eb, 126));
-#pragma unroll
-      for (int f = 0; f < 32; ++f) {
-        float lv;
-        put6(lo, f, e2m3_round(xp[f] * invb, &lv));
-      }
-      const size_t gl = (size_t)G * 256;  // lane group G's 16-byte slots in each 1 KiB piece
-      *reinterpret_cast<u32x4*>(xq + ((size_t)s * 3 + 0) * ostep + gl) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<u32x4*>(xq + ((size_t)s * 3 + 1) * ostep + gl) = u32x4{hi[4], hi[5], lo[0], lo[1]};
-      *reinterpret_cast<u32x4*>(xq + ((size_t)s * 3 + 2) * ostep + gl) = u32x4{lo[2], lo[3], lo[4], lo[5]};
-      *reinterpret_cast<unsigned*>(xs + (size_t)s * nblk * 256 + (size_t)G * 64) =
-          (unsigned)(ea + 127) | ((unsigned)(eb + 127) << 8);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(x + 32 * g + 8 * q);
+    v[4 * q] = c[0];
+    v[4 * q + 1] = c[1];
+    v[4 * q + 2] = c[2];
+    v[4 * q + 3] = c[3];
   }
+  float xp[32];  // x' in operand order: field f <- column 4 (f % 8) + f / 8 of the block
+  float m = 0.f;
+#pragma unroll
+  for (int f = 0; f < 32; ++f) {
+    const int col = 4 * (f & 7) + (f >> 3);
+    const unsigned pair = v[col >> 1];
+    xp[f] = alpha * ((col & 1) ? bf16hi_to_f32(pair) : bf16lo_to_f32(pair));
+    m = fmaxf(m, fabsf(xp[f]));
+  }
+  int ea = m > 0.f ? e2m3_block_exp(m) : 0;
+  ea = max(-126, min(127, ea));
+  const float sa = pow2f(ea), inva = pow2f(-min(ea, 126));
+  unsigned hi[6] = {0, 0, 0, 0, 0, 0}, lo[6] = {0, 0, 0, 0, 0, 0};
+  float rm = 0.f;
+#pragma unroll
+  for (int f = 0; f < 32; ++f) {
+    float hv;
+    put6(hi, f, e2m3_round(xp[f] * inva, &hv));
+    xp[f] -= hv * sa;                        // remainder
+    rm = fmaxf(rm, fabsf(xp[f]));
+  }
+  int eb = rm > 0.f ? e2m3_block_exp(rm) : ea;
+  eb = max(-126, min(127, eb));
+  const float invb = pow2f(-min(eb, 126));
+#pragma unroll
+  for (int f = 0; f < 32; ++f) {
+    float lv;
+    put6(lo, f, e2m3_round(xp[f] * invb, &lv));
+  }
+  unsigned char* q = a.xq[p] + pbase;
+  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 0) * ostep) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 1) * ostep) = u32x4{hi[4], hi[5], lo[0], lo[1]};
+  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 2) * ostep) = u32x4{lo[2], lo[3], lo[4], lo[5]};
+  *reinterpret_cast<unsigned*>(a.xs[p] + ((size_t)s * nblk + tb) * 256 + (size_t)lane * 4) =
+      (unsigned)(ea + 127) | ((unsigned)(eb + 127) << 8);
 }
 
 // Dynamic LDS one workgroup may use on the current device, capped at one compute unit's.
@@ -570,12 +575,18 @@ size_t split_workspace_bytes(int64_t M, int64_t d_in) {
   return b + q + c;
 }
 
-hipError_t launch_split_act(const SplitActArgs& a, int ntok, hipStream_t stream) {
-  if (ntok <= 0 || a.nprob <= 0 || a.nprob > kMaxProblems || a.lo < 0 ||
-      a.lo + ntok > kSplitMaxM || (a.tok_base & 15) != 0)
+hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream) {
+  if (a.nprob <= 0 || a.nprob > kMaxProblems || a.lo < 0 || a.hi <= a.lo || a.hi > kSplitMaxM ||
+      (a.tok_base & 15) != 0)
     return hipErrorInvalidValue;
+  int max_steps = 0;
+  for (int q = 0; q < a.nprob; ++q) max_steps = max(max_steps, a.d_in[q] / 128);
+  const int nsq = (max_steps + kActSteps - 1) / kActSteps;
+  const int ntb = (a.hi - 1) / 16 - a.lo / 16 + 1;
+  if (nsq < 1) return hipErrorInvalidValue;
   clear_stale_error();
-  hipLaunchKernelGGL(split_act_kernel, dim3(ntok, a.nprob), dim3(kActThreads), 0, stream, a);
+  hipLaunchKernelGGL(split_act_kernel, dim3(ntb * nsq, a.nprob), dim3(kActThreads), 0, stream, a,
+                     nsq);
   return hipGetLastError();
 }
 
