@@ -130,6 +130,8 @@ struct SplitProblem {
 struct SplitWave {
   int32_t tile[2];                       // 16-token block (relative) of the dense tiles, -1 none
   int32_t slot[kSplitMaxGroups][2];      // slot group g: the variant slot of tile i's pair, -1 none
+  int32_t copier;                        // 0..3: this wave issues copy share `copier`, -1 none
+  int32_t pad_;
 };
 
 struct SplitArgs {

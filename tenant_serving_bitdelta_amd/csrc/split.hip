@@ -169,14 +169,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   const int j = lane & 15, g = lane >> 4;
 
   // ---- direct copies (global -> LDS), `ahead` steps ahead, into stage s % nst ------------------
-  // Waves 0-3 (one per SIMD) issue every copy, 16 each per step, spread over their sign phase,
-  // so that the other wave of each SIMD is never held up by a full memory-instruction queue.
+  // Four waves (the host picks the less loaded wave of each SIMD) issue every copy, 16 each per
+  // step, spread over their sign phase, so that the other wave of each SIMD is never held up by
+  // a full memory-instruction queue.
   // W_base: copy b = 8*wave + u (of 32) moves rows 4b..4b+3 of the block for one step, 256 bytes
   // each, so every 4 consecutive lanes read 64 contiguous bytes.  Lane L writes LDS slot
   // (row 4b + L/16, 16-byte position L%16) and fetches 16-byte column chunk position ^ (row%16):
   // the XOR swizzle keeps the MFMA operand reads below conflict-free.
-  const bool copier = wave < kCopyWaves;
-  const int cw = copier ? wave : 0;
+  const int cw_raw = a.wv[wave].copier;
+  const bool copier = cw_raw >= 0;
+  const int cw = copier ? cw_raw : 0;
   const rsrc_t wrs = make_rsrc(P.w + (size_t)row0 * d_in);
   unsigned woff[8];
 #pragma unroll
@@ -595,8 +597,14 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
       a.nslots < 0 || a.nslots > kMaxSlots || a.nprob < 1 || a.nprob > kMaxProblems ||
       nd < 1 || nd > 2 || ng < 0 || ng > kSplitMaxGroups)
     return hipErrorInvalidValue;
+  unsigned copy_shares = 0;
   for (int w = 0; w < kWaves; ++w) {
     const SplitWave& W = a.wv[w];
+    if (W.copier < -1 || W.copier >= kCopyWaves) return hipErrorInvalidValue;
+    if (W.copier >= 0) {
+      if (copy_shares >> W.copier & 1u) return hipErrorInvalidValue;
+      copy_shares |= 1u << W.copier;
+    }
     for (int i = 0; i < 2; ++i)
       if (W.tile[i] >= kSplitMaxM / 16 || (i >= nd && W.tile[i] >= 0)) return hipErrorInvalidValue;
     for (int q = 0; q < kSplitMaxGroups; ++q)
@@ -606,6 +614,7 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
         if (slot >= 0 && (q >= ng || i >= nd || W.tile[i] < 0)) return hipErrorInvalidValue;
       }
   }
+  if (copy_shares != (1u << kCopyWaves) - 1u) return hipErrorInvalidValue;  // every copy issued
   const int lds = lds_limit();
   const unsigned stage = kWStage + (unsigned)a.nslots * kSSlot;
   int nst = lds / (int)stage;
