@@ -341,7 +341,8 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
 bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
                           const std::vector<Segment>& segs, int y_f32, void* workspace,
                           hipStream_t st) {
-  // workspace, per problem: bf16 pieces, fp6 pieces, block scales
+  // workspace: per problem bf16 pieces, fp6 pieces, block scales; then every problem's share of
+  // partial slots, then of split counters
   const int Mp = (int)((M + 15) / 16 * 16);
   std::vector<unsigned char*> xb(np), xq(np), xs(np);
   size_t off = 0;
@@ -354,6 +355,13 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
     xs[p] = base + bb + qb;
     off += bb + qb + cb;
   }
+  const size_t slot_bytes = bd::split_slot_bytes(M);
+  const int slots_total = np * bd::kSplitSlotsPerLinear;  // counters: as many
+  float* partial = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + off);
+  // slot_bytes is a multiple of 256, so the slots of all problems end on a 256-byte boundary
+  int32_t* counter = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + off +
+                                                (size_t)slots_total * slot_bytes);
+  const int C = bd::split_compute_units() / 8;
   // problems with longer rows first, so the longest workgroups do not form the tail
   std::vector<int> order(np);
   for (int p = 0; p < np; ++p) order[p] = p;
@@ -402,6 +410,25 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
       const int pn = std::min(np - p0, bd::kMaxProblems);
       a.nprob = pn;
       act.nprob = pn;
+      bd::SplitShape sh;
+      memset(&sh, 0, sizeof(sh));
+      sh.np = pn;
+      sh.C = C;
+      sh.Mp = Mp;
+      sh.nslots = a.nslots;
+      sh.slots_avail = std::min(slots_total, bd::kMaxProblems * bd::kSplitSlotsPerLinear) / 8;
+      for (int q = 0; q < pn; ++q) {
+        const bitdelta_problem& P = probs[order[p0 + q]];
+        sh.ns[q] = (int)(P.d_in / 128);
+        sh.nb[q] = (int)((P.d_out + bd::kSplitRows - 1) / bd::kSplitRows);
+      }
+      bd::SplitSched& H = a.sch;
+      H = bd::split_schedule(sh);
+      H.slot_bytes = (uint32_t)slot_bytes;
+      H.partial = partial;
+      H.counter = counter;
+      act.counter = counter;
+      act.ncounter = 8 * H.nsplit;
       for (int q = 0; q < pn; ++q) {
         const int p = order[p0 + q];
         const bitdelta_problem& P = probs[p];

@@ -134,17 +134,108 @@ struct SplitWave {
   int32_t pad_;
 };
 
+// Work schedule of a split launch, the same for each of the 8 XCDs (XCD x serves the x-th eighth
+// of every linear's 128-row blocks, its "units"; units are counted with the largest eighth,
+// ceil(nblocks / 8)).  The grid's per-XCD list first holds one piece per unit, linear by linear:
+// steps [0, head) of each of its first units, all but the last `pooled` ones.  Then the pool:
+// linear by linear, the steps [head, nsteps) of its cut units (head < nsteps) in pieces of
+// `sigma` steps, then its pooled units whole, also in pieces of `sigma` steps; pieces of the
+// same steps of different units come one after another, so they run side by side and share
+// the activations in L2.  A unit done in several pieces is "split": each piece leaves its fp32
+// sums in a partial slot, and the piece that finishes last adds the slots in piece order and
+// writes y.
+struct SplitSched {
+  int32_t head[kMaxProblems];            // steps of the first piece of every unit of linear q
+  int32_t pooled[kMaxProblems];          // trailing units of linear q done in the pool
+  int32_t sigma;                         // pool piece length in K steps (>= 1)
+  int32_t nheads, npool;                 // list lengths per XCD
+  int32_t nsplit, nslot;                 // split units and partial slots per XCD
+  uint32_t slot_bytes;                   // bytes of one partial slot (128 rows x 4 x Mp)
+  float* partial;                        // [8][nslot] partial slots
+  int32_t* counter;                      // [8][nsplit] finished pieces per split unit
+};
+
+// Piece kk of an XCD's list under schedule H, for linears with ns[q] K steps and nb[q] row
+// blocks (q < nprob): linear p (-1 past the end), unit lrb of the XCD's eighth, K steps [k0, k1);
+// for a split unit (nparts > 1) its piece index, split counter sid and first partial slot.
+struct SplitPiece {
+  int p, lrb, k0, k1, nparts, part, sid, slot0;
+};
+__host__ __device__ inline SplitPiece split_piece(const SplitSched& H, int nprob, const int* ns,
+                                                  const int* nb, int kk) {
+  SplitPiece r = {-1, 0, 0, 0, 1, 0, 0, 0};
+  const bool in_pool = kk >= H.nheads;
+  if (in_pool) kk -= H.nheads;
+  int sid_base = 0, slot_base = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxProblems; ++q) {
+    if (q < nprob) {
+      const int cnt = (nb[q] + 7) >> 3;                  // units of the largest eighth
+      const int nh = cnt - H.pooled[q];                  // units with a head piece
+      const int tail = ns[q] - H.head[q];
+      const int tp = tail > 0 ? (tail + H.sigma - 1) / H.sigma : 0;  // pool pieces of a cut unit
+      const int pp = (ns[q] + H.sigma - 1) / H.sigma;                // pieces of a pooled unit
+      const int ncut = tail > 0 ? nh : 0;
+      if (r.p < 0) {
+        if (!in_pool) {
+          if (kk < nh) {
+            r.p = q; r.lrb = kk; r.k0 = 0; r.k1 = H.head[q];
+            if (tail > 0) {
+              r.nparts = 1 + tp; r.part = 0; r.sid = sid_base + kk; r.slot0 = slot_base + kk * r.nparts;
+            }
+          } else {
+            kk -= nh;
+          }
+        } else if (kk < ncut * tp) {  // same steps of the cut units one after another
+          const int jj = kk / ncut, u = kk - jj * ncut;
+          r.p = q; r.lrb = u; r.k0 = H.head[q] + jj * H.sigma;
+          r.k1 = r.k0 + H.sigma < ns[q] ? r.k0 + H.sigma : ns[q];
+          r.nparts = 1 + tp; r.part = 1 + jj; r.sid = sid_base + u; r.slot0 = slot_base + u * r.nparts;
+        } else {
+          kk -= ncut * tp;
+          if (kk < H.pooled[q] * pp) {
+            const int jj = kk / H.pooled[q], u = kk - jj * H.pooled[q];
+            r.p = q; r.lrb = nh + u; r.k0 = jj * H.sigma;
+            r.k1 = r.k0 + H.sigma < ns[q] ? r.k0 + H.sigma : ns[q];
+            r.nparts = pp; r.part = jj; r.sid = sid_base + ncut + u;
+            r.slot0 = slot_base + ncut * (1 + tp) + u * pp;
+          } else {
+            kk -= H.pooled[q] * pp;
+          }
+        }
+      }
+      sid_base += ncut + H.pooled[q];
+      slot_base += ncut * (1 + tp) + H.pooled[q] * pp;
+    }
+  }
+  return r;
+}
+
 struct SplitArgs {
   SplitProblem prob[kMaxProblems];
   int nprob, nslots, y_f32;
   int tok_base;                          // first token of this launch's 16-token blocks
   int lo, hi;                            // tokens [tok_base + lo, tok_base + hi) are this launch's
   int Mp, pad_;                          // token count of the layouts (call's M rounded up to 16)
+  SplitSched sch;
   SplitWave wv[8];
   int8_t token_slot[kSplitMaxM];         // slot of token tok_base + t (-1 = base model); read per lane
 };
 // nd: dense tiles per wave (1 or 2); ng: slot groups per wave (at most kSplitMaxGroups).
 hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream);
+
+// What the schedule of a split launch depends on: the linears (in launch order) with ns K steps
+// and nb row blocks, C compute units per XCD, the batch Mp, the launch's variant count and the
+// partial slots per XCD the workspace holds.
+struct SplitShape {
+  int np, C, Mp, nslots, slots_avail;
+  int ns[kMaxProblems], nb[kMaxProblems];
+};
+// head, pooled, sigma and the list counts (partial, counter and slot_bytes are left 0).
+SplitSched split_schedule(const SplitShape& sh);
+// The simulated makespan of a schedule, in K steps (for tests).
+double split_schedule_makespan(const SplitShape& sh, const SplitSched& h);
+int split_compute_units();  // compute units of the current device
 
 struct SplitActArgs {
   const uint16_t* x[kMaxProblems];     // bf16 [M][d_in] row-major (the caller's activations)
@@ -154,12 +245,18 @@ struct SplitActArgs {
   const float* alpha[kMaxProblems][kMaxSlots];
   int d_in[kMaxProblems];
   int Mp, tok_base, lo, hi, nprob, pad_;  // tokens [tok_base + lo, tok_base + hi)
+  int32_t* counter;                    // out: ncounter split counters set to zero
+  int ncounter, pad2_;
   int8_t token_slot[kSplitMaxM];       // slot of token tok_base + t (-1 = base model); read per lane
 };
 hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream);
-// Workspace of one linear: bf16 pieces, fp6 pieces, scales; each part a multiple of 256 bytes.
+// Workspace of one linear: bf16 pieces, fp6 pieces, scales, and its share of the call's partial
+// slots and split counters (kSplitSlotsPerLinear of each); each part a multiple of 256 bytes.
+constexpr int kSplitSlotsPerLinear = 128;
 size_t split_workspace_bytes(int64_t M, int64_t d_in);
 void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq_bytes,
                            size_t* xs_bytes);
+size_t split_partial_bytes(int64_t M);   // one linear's share of partial slots and counters
+size_t split_slot_bytes(int64_t M);      // one partial slot
 
 }  // namespace bd

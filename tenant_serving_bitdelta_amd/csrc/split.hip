@@ -109,6 +109,9 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned voff, unsigned char* ld
 // 16 or 4 bytes from a raw buffer; an offset at or past kOob reads as zero without touching
 // memory.
 constexpr unsigned kOob = 0x80000000u;
+// cache policy of a buffer access that is coherent at device scope (it bypasses the compute
+// unit's cache; the same policy as a relaxed device-scope atomic load or store)
+constexpr int kDeviceCoherent = 16;
 __device__ __forceinline__ u32x4 load16(rsrc_t r, unsigned voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
@@ -136,27 +139,27 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
                                                             int nst) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  // ---- which linear and which 128-row block (wave-uniform) -----------------------------------
-  // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).  XCD x
-  // serves the x-th eighth of every linear's row blocks, consecutively, so the workgroups that
-  // run side by side on one XCD (sharing its L2) read the same activations at the same time.
+  // ---- which piece: linear, 128-row block and K steps (wave-uniform) ---------------------------
+  // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), and each
+  // XCD takes its list (the schedule above) in order.  XCD x serves the x-th eighth of every
+  // linear's row blocks, so the workgroups that run side by side on one XCD (sharing its L2) read
+  // the same activations at the same time.
+  const SplitSched& H = a.sch;
   const int xcd = blockIdx.x & 7;
-  int kk = blockIdx.x >> 3, p = -1, rb = 0;
+  int ns_q[kMaxProblems], nb_q[kMaxProblems];
 #pragma unroll
   for (int q = 0; q < kMaxProblems; ++q) {
-    if (q < a.nprob && p < 0) {
-      const int n = a.prob[q].nblocks;
-      const int lo = (xcd * n) >> 3, len = (((xcd + 1) * n) >> 3) - lo;
-      if (kk < len) {
-        p = q;
-        rb = lo + kk;
-      } else {
-        kk -= len;
-      }
-    }
+    ns_q[q] = q < a.nprob ? a.prob[q].d_in / kKS : 0;
+    nb_q[q] = q < a.nprob ? a.prob[q].nblocks : 0;
   }
-  if (p < 0) return;  // this XCD's list is shorter than the longest one
+  const SplitPiece pc0 = split_piece(H, a.nprob, ns_q, nb_q, (int)(blockIdx.x >> 3));
+  const int p = pc0.p, lrb = pc0.lrb, k0 = pc0.k0, k1 = pc0.k1, nparts = pc0.nparts,
+            part = pc0.part, sid = pc0.sid, slot0 = pc0.slot0;
+  if (p < 0) return;  // past the end of the list
   const SplitProblem& P = a.prob[p];
+  const int rb_lo = (xcd * P.nblocks) >> 3;
+  if (lrb >= (((xcd + 1) * P.nblocks) >> 3) - rb_lo) return;  // this XCD's eighth is shorter
+  const int rb = rb_lo + lrb;
   const int d_in = P.d_in, d_out = P.d_out;
   const int row0 = rb * kRows;
   const int nslots = a.nslots;
@@ -265,16 +268,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   // vector-memory instructions per step that are activation loads
   constexpr int kX = 8 * ND;
 
-  // ---- prologue: stages 0..ahead-1 and the activations of step 0 -------------------------------
+  // ---- prologue: steps k0..k0+ahead-1 into stages 0..ahead-1, the activations of step k0 ------
   if (copier)
-    for (int s = 0; s < ahead && s < nsteps; ++s)
+    for (int r = 0; r < ahead && k0 + r < k1; ++r)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) copy(k, s, (unsigned)s * stage_bytes);
+      for (int k = 0; k < 16; ++k) copy(k, k0 + r, (unsigned)r * stage_bytes);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < ND; ++i) load_xq(i, 0);
+  for (int i = 0; i < ND; ++i) load_xq(i, (unsigned)k0);
 #pragma unroll
-  for (int i = 0; i < ND; ++i) load_xb(i, 0);
+  for (int i = 0; i < ND; ++i) load_xb(i, (unsigned)k0);
   __builtin_amdgcn_sched_barrier(0);
   SPLIT_VMCNT(cmin63<kX>());
   raw_barrier();
@@ -351,11 +354,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     }
   };
 
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = k0; s < k1; ++s) {
     // Each activation operand is reloaded for step s+1 right after its last use in step s, so
     // every load has most of a step to arrive.
-    const unsigned knext = (unsigned)min(s + 1, nsteps - 1);
-    sign_phase(copier && s + ahead < nsteps, s + ahead, st_next, st);
+    const unsigned knext = (unsigned)min(s + 1, k1 - 1);
+    sign_phase(copier && s + ahead < k1, s + ahead, st_next, st);
 #pragma unroll
     for (int i = 0; i < ND; ++i) load_xq(i, knext);
     base_phase(knext, st);
@@ -373,6 +376,52 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     if (st == ring) st = 0;
     st_next += stage_bytes;
     if (st_next == ring) st_next = 0;
+  }
+
+  // ---- split unit: leave the sums in this piece's slot; the last piece adds all slots ------------
+  // A slot holds, per dense tile i of the launch and row tile rt, the 64 lanes' f32x4 in lane
+  // order, so each wave reads back exactly what the same wave of another piece wrote.  Every
+  // piece of a unit runs on the same XCD, whose L2 all its compute units share: the slots are
+  // written and read with device-coherent accesses (which skip the compute unit's own cache),
+  // each wave waits until its stores are done before the workgroup counts itself in, and the
+  // workgroup that brings the count to nparts adds the slots in piece order (its own sums from
+  // registers, so the order, and the result, do not depend on which piece finished last).
+  if (nparts > 1) {
+    const rsrc_t prs = make_rsrc(reinterpret_cast<unsigned char*>(H.partial) +
+                                 (size_t)(xcd * H.nslot + slot0) * H.slot_bytes);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      if (!dreal[i]) continue;
+      const unsigned o = (unsigned)part * H.slot_bytes +
+                         (unsigned)a.wv[wave].tile[i] * (kRT * 1024) + (unsigned)lane * 16;
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][rt]), prs,
+                                               o + rt * 1024, 0, kDeviceCoherent);
+    }
+    SPLIT_VMCNT(0);
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(smem);
+    if (tid == 0)
+      flag[0] = __hip_atomic_fetch_add(H.counter + xcd * H.nsplit + sid, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (flag[0] != nparts - 1) return;  // workgroup-uniform: another piece finishes this unit
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      if (!dreal[i]) continue;
+      const unsigned o = (unsigned)a.wv[wave].tile[i] * (kRT * 1024) + (unsigned)lane * 16;
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int pc = 0; pc < nparts; ++pc)
+          v += pc == part ? acc[i][rt]
+                          : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                prs, (unsigned)pc * H.slot_bytes + o + rt * 1024, 0,
+                                kDeviceCoherent));
+        acc[i][rt] = v;
+      }
+    }
   }
 
   // ---- epilogue: y = accumulators ---------------------------------------------------------------
@@ -460,6 +509,8 @@ __device__ __forceinline__ void put6(unsigned* w, int f, unsigned c) {
 }
 
 __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActArgs a, int nsq) {
+  if (blockIdx.x == 0 && blockIdx.y == 0)  // the split counters of the launch that follows
+    for (int c = threadIdx.x; c < a.ncounter; c += kActThreads) a.counter[c] = 0;
   const int p = blockIdx.y;
   const int d_in = a.d_in[p], nsteps = d_in / 128;
   const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
@@ -571,15 +622,24 @@ void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq
   *xs_bytes = round256(mp * (size_t)d_in / 8);       // 4 bytes per token and 32 columns
 }
 
+size_t split_slot_bytes(int64_t M) {
+  return (size_t)((M + 15) / 16) * 16 * kSplitRows * 4;
+}
+
+size_t split_partial_bytes(int64_t M) {
+  return round256((size_t)kSplitSlotsPerLinear * split_slot_bytes(M)) +
+         round256((size_t)kSplitSlotsPerLinear * 4);
+}
+
 size_t split_workspace_bytes(int64_t M, int64_t d_in) {
   size_t b, q, c;
   split_workspace_parts(M, d_in, &b, &q, &c);
-  return b + q + c;
+  return b + q + c + split_partial_bytes(M);
 }
 
 hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream) {
   if (a.nprob <= 0 || a.nprob > kMaxProblems || a.lo < 0 || a.hi <= a.lo || a.hi > kSplitMaxM ||
-      (a.tok_base & 15) != 0)
+      (a.tok_base & 15) != 0 || a.ncounter < 0 || (a.ncounter > 0 && !a.counter))
     return hipErrorInvalidValue;
   int max_steps = 0;
   for (int q = 0; q < a.nprob; ++q) max_steps = max(max_steps, a.d_in[q] / 128);
@@ -620,17 +680,30 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
   int nst = lds / (int)stage;
   nst = nst > 4 ? 4 : nst;
   if (nst < 2) return hipErrorInvalidConfiguration;
-  // grid: 8 XCD lists, each as long as the longest (see the block map in the kernel)
-  int longest = 0;
-  for (int x = 0; x < 8; ++x) {
-    int len = 0;
-    for (int q = 0; q < a.nprob; ++q) {
-      if (a.prob[q].nblocks < 1) return hipErrorInvalidValue;
-      len += (((x + 1) * a.prob[q].nblocks) >> 3) - ((x * a.prob[q].nblocks) >> 3);
-    }
-    longest = len > longest ? len : longest;
+  // the schedule must describe the lists the kernel walks (see the piece map in the kernel)
+  const SplitSched& H = a.sch;
+  if (H.sigma < 1) return hipErrorInvalidValue;
+  int nheads = 0, npool = 0, nsplit = 0, nslot = 0;
+  for (int q = 0; q < a.nprob; ++q) {
+    const SplitProblem& P = a.prob[q];
+    if (P.nblocks < 1 || P.d_in < kKS || P.d_in % kKS != 0) return hipErrorInvalidValue;
+    const int ns = P.d_in / kKS, cnt = (P.nblocks + 7) >> 3;
+    if (H.head[q] < 1 || H.head[q] > ns || H.pooled[q] < 0 || H.pooled[q] > cnt)
+      return hipErrorInvalidValue;
+    const int nh = cnt - H.pooled[q], tail = ns - H.head[q];
+    const int tp = tail > 0 ? (tail + H.sigma - 1) / H.sigma : 0;
+    const int pp = (ns + H.sigma - 1) / H.sigma;
+    const int ncut = tail > 0 ? nh : 0;
+    nheads += nh;
+    npool += ncut * tp + H.pooled[q] * pp;
+    nsplit += ncut + H.pooled[q];
+    nslot += ncut * (1 + tp) + H.pooled[q] * pp;
   }
-  const int nblocks = 8 * longest;
+  if (nheads != H.nheads || npool != H.npool || nsplit != H.nsplit || nslot != H.nslot)
+    return hipErrorInvalidValue;
+  if (nslot > 0 && (!H.partial || !H.counter || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
+    return hipErrorInvalidValue;
+  const int nblocks = 8 * (nheads + npool);
   if (nd == 1) {
     if (ng <= 1) return launch_nd_ng<1, 1>(a, nblocks, stage, nst, stream);
     if (ng <= 2) return launch_nd_ng<1, 2>(a, nblocks, stage, nst, stream);

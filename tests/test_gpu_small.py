@@ -343,3 +343,42 @@ def test_split_many_short_runs(run):
          "token_variant": ids.astype(np.int32)}
     for out in ("bf16", "f32"):
         run_matmul(c, "split", out)
+
+
+@pytest.mark.parametrize("d_out,d_in,m,nv,dist", [(200, 8192, 40, 5, "uniform"),
+                                                  (136, 4096, 256, 14, "zipf"),
+                                                  (1000, 16384, 17, 3, "uniform")])
+def test_split_k_pieces(d_out, d_in, m, nv, dist):
+    """Few 128-row blocks with many K steps: the launch cuts each block's K range into pieces
+    that run on different compute units and meet in fp32 partial slots (the piece that finishes
+    last adds them in piece order), so the result must match the oracle and repeat bit for bit."""
+    c = WL.linear_case(seed=d_out + d_in + m, d_out=d_out, d_in=d_in, m=m, num_variants=nv,
+                       dist=dist, base_frac=0.1, zero_frac=0.01)
+    for out in ("bf16", "f32"):
+        y1, *_ = run_matmul(c, "split", out)
+        y2, *_ = run_matmul(c, "split", out)
+        assert torch.equal(y1, y2), "split result differs between identical calls"
+
+
+def test_split_k_pieces_grouped():
+    """Linears of different K in one launch: long ones cut into a head and pool pieces."""
+    rng = np.random.default_rng(91)
+    m, nv = 48, 4
+    ids = rng.integers(-1, nv, size=m).astype(np.int32)
+    perm, offs, segv = bd.plan_segments(ids, nv)
+    shapes = [(384, 2048), (256, 12288), (130, 4096)]
+    probs, refs = [], []
+    for d_out, d_in in shapes:
+        w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
+        deltas = [rng.laplace(0, 4e-4, size=(d_out, d_in)).astype(np.float32) for _ in range(nv)]
+        x_bits = WL.f32_to_bf16_bits(rng.normal(size=(m, d_in)).astype(np.float32))
+        var_gpu = gpu_compress(deltas)
+        y = torch.empty((m, d_out), dtype=torch.float32, device="cuda")
+        probs.append((bf16_dev(x_bits[perm]), bf16_dev(w_bits), y, var_gpu))
+        refs.append(O.matmul_ref(O.bf16_bits_to_f64(x_bits)[perm], O.bf16_bits_to_f64(w_bits),
+                                 [O.compress_ref(d) for d in deltas], offs, segv))
+    bd.matmul_grouped(probs, offs, segv, path="split", out_dtype="f32")
+    torch.cuda.synchronize()
+    for (_, _, y, _), y_ref in zip(probs, refs):
+        rel = row_rel_l2(y.cpu().numpy().astype(np.float64), y_ref)
+        assert rel.max() <= 5e-3, f"row rel L2 {rel.max():.3e}"
