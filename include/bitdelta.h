@@ -66,8 +66,9 @@ typedef enum {
   BITDELTA_PATH_GEMV = 1,    /* fp32 reconstruction in registers, VALU; M <= 4                 */
   BITDELTA_PATH_STREAM = 2,  /* decode: base and sign sums both as bf16 MFMA; no workspace     */
   BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
-  BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp8 MFMA on an exact
-                              * two-term fp8 split of x; needs workspace and tiled sign words  */
+  BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp6 MFMA on a
+                              * two-term fp6 split of alpha * x (per-32-column power-of-two
+                              * scales); needs workspace and tiled sign words                 */
 } bitdelta_path;
 
 /* One compressed variant of one weight matrix: the output of bitdelta_compress. */
@@ -158,8 +159,12 @@ bitdelta_status bitdelta_plan_segments(const int32_t* token_variant, int64_t M,
  * bitdelta_matmul_workspace_bytes — device workspace one linear (one problem) of a matmul call
  * on `path` needs, for a batch of M tokens and input width d_in (a multiple of 256 bytes; 0 when
  * the path needs none).  AUTO reports what the path AUTO would pick for M needs.  A grouped call
- * needs the sum over its problems.  The SPLIT path writes each token's activations there as two
- * fp8 terms (2 * d_in bytes) plus a scale code (4 bytes); M = 0 or invalid arguments give 0.
+ * needs the sum over its problems.  The SPLIT path keeps there, per token (M rounded up to 16),
+ * a bf16 copy of its activations in operand order (2 * d_in bytes), the two fp6 terms of
+ * alpha * x (1.5 * d_in bytes) and one scale word per 32 columns (d_in / 8 bytes), and, per
+ * linear, 128 fp32 partial-sum slots of 128 rows (512 bytes per token each) plus 128 counters,
+ * which the launch uses when it splits a 128-row block's K range over several compute units.
+ * M = 0 or invalid arguments give 0.
  */
 size_t bitdelta_matmul_workspace_bytes(int64_t M, int64_t d_in, int32_t path);
 
