@@ -344,16 +344,17 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
   // workspace: per problem bf16 pieces, fp6 pieces, block scales; then every problem's share of
   // partial slots, then of split counters
   const int Mp = (int)((M + 15) / 16 * 16);
-  std::vector<unsigned char*> xb(np), xq(np), xs(np);
+  std::vector<unsigned char*> xb(np), xq(np), xs(np), xc(np);
   size_t off = 0;
   for (int p = 0; p < np; ++p) {
     unsigned char* base = static_cast<unsigned char*>(workspace) + off;
-    size_t bb, qb, cb;
-    bd::split_workspace_parts(M, probs[p].d_in, &bb, &qb, &cb);
+    size_t bb, qb, cb, kb;
+    bd::split_workspace_parts(M, probs[p].d_in, &bb, &qb, &cb, &kb);
     xb[p] = base;
     xq[p] = base + bb;
     xs[p] = base + bb + qb;
-    off += bb + qb + cb;
+    xc[p] = base + bb + qb + cb;
+    off += bb + qb + cb + kb;
   }
   const size_t slot_bytes = bd::split_slot_bytes(M);
   const int slots_total = np * bd::kSplitSlotsPerLinear;  // counters: as many
@@ -436,11 +437,13 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
         act.xb[q] = xb[p];
         act.xq[q] = xq[p];
         act.xs[q] = xs[p];
+        act.xc[q] = reinterpret_cast<float*>(xc[p]);
         act.d_in[q] = (int)P.d_in;
         bd::SplitProblem& S = a.prob[q];
         S.x = xb[p];
         S.xq = xq[p];
         S.xs = xs[p];
+        S.xc = reinterpret_cast<const float*>(xc[p]);
         S.w = static_cast<const uint16_t*>(P.w_base);
         S.y = P.y;
         S.d_out = (int)P.d_out;

@@ -118,6 +118,7 @@ struct SplitProblem {
   const unsigned char* x;     // bf16 activations in base-operand order (prologue layout)
   const unsigned char* xq;    // fp6 hi/lo terms of alpha * x in sign-operand order
   const unsigned char* xs;    // E8M0 block scales of the two terms
+  const float* xc;            // [nsteps][Mp] per step and token: sum of x' over the unsigned columns
   const uint16_t* w;
   void* y;                    // [M][d_out] of the whole call
   int d_out, d_in;
@@ -242,6 +243,7 @@ struct SplitActArgs {
   unsigned char* xb[kMaxProblems];     // out: bf16 in base-operand order
   unsigned char* xq[kMaxProblems];     // out: fp6 hi/lo terms of alpha * x in sign-operand order
   unsigned char* xs[kMaxProblems];     // out: their block scales
+  float* xc[kMaxProblems];             // out: per step and token, the correction sums
   const float* alpha[kMaxProblems][kMaxSlots];
   int d_in[kMaxProblems];
   int Mp, tok_base, lo, hi, nprob, pad_;  // tokens [tok_base + lo, tok_base + hi)
@@ -250,12 +252,13 @@ struct SplitActArgs {
   int8_t token_slot[kSplitMaxM];       // slot of token tok_base + t (-1 = base model); read per lane
 };
 hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream);
-// Workspace of one linear: bf16 pieces, fp6 pieces, scales, and its share of the call's partial
-// slots and split counters (kSplitSlotsPerLinear of each); each part a multiple of 256 bytes.
+// Workspace of one linear: bf16 pieces, fp6 pieces, scales, correction sums, and its share of
+// the call's partial slots and split counters (kSplitSlotsPerLinear of each); each part a
+// multiple of 256 bytes.
 constexpr int kSplitSlotsPerLinear = 128;
 size_t split_workspace_bytes(int64_t M, int64_t d_in);
 void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq_bytes,
-                           size_t* xs_bytes);
+                           size_t* xs_bytes, size_t* xc_bytes);
 size_t split_partial_bytes(int64_t M);   // one linear's share of partial slots and counters
 size_t split_slot_bytes(int64_t M);      // one partial slot
 

@@ -8,7 +8,7 @@
 // The two sums share one fp32 accumulator per (token, row); W_eff is never formed:
 //   * base sum: bf16 x bf16 MFMA (v_mfma_f32_16x16x32_bf16) over DENSE 16-token tiles of the
 //     batch (the base weights are the same for every token);
-//   * sign sum: v_mfma_scale_f32_16x16x128_f8f6f4 with the signs as fp4 (e2m1) +-1.0 and the
+//   * sign sum: v_mfma_scale_f32_16x16x128_f8f6f4 with the signs as fp4 (e2m1) and the
 //     variant-scaled activations x' = alpha_v * x (fp32 products) as two fp6 (e2m3) terms,
 //     x' ~ 2^a * hi + 2^b * lo, with one pair of power-of-two scales (a, b) per token and
 //     32-column block (the E8M0 block scales of the instruction): a puts the block's largest
@@ -18,18 +18,23 @@
 //     2^-4 of the block's largest |x'|: about 2^-8 of the block maximum, the size of a bf16
 //     rounding of x'.  The fp4 x fp6 instruction issues at twice the rate of fp4 x fp8, so the
 //     two terms cost what one fp8 term would.  One instruction covers a (dense tile, variant)
-//     pair: the tile's tokens of other variants are zeroed in registers, so the products add
-//     straight into the dense tile's accumulators.
-// A sign word of 32 bits becomes the fp4 operand with one shift and one 3-input bit operation
-// per 8 weights.
+//     pair: the tile's tokens of other variants get block scale 2^-127, so their products
+//     vanish and the pair's products add straight into the dense tile's accumulators.
 //
-// K order.  Inside one 128-wide K step the instruction's lane group G (lanes 16G..16G+15) holds
-// K positions 32G..32G+31 of both operands.  In the fp4 operand nibble n of dword d is position
-// 32G + 8d + n; that position is mapped to weight column 32G + 4n + d, i.e. bit 4n + d of sign
-// word G of the step, so dword d of the operand is ((word << (3 - d)) & 0x88888888) ^
-// 0xAAAAAAAA (0x2 = +1.0, 0xA = -1.0).  In the fp6 operand field f (bits 6f..6f+5 of six
-// dwords) is position 32G + f; the prologue writes column 32G + 4 (f % 8) + f / 8 there, so both
-// operands agree on every product.  The block scale of lane group G covers columns 32G..32G+31.
+// K order and the sign operand.  Inside one 128-wide K step the instruction's lane group G
+// (lanes 16G..16G+15) holds K positions 32G..32G+31 of both operands.  In the fp4 operand
+// nibble n of dword d is position 32G + 8d + n, mapped to weight column 32d + 4n + G: bit
+// 4n + G of sign word d of the step.  So lane group G keeps only the bits at one place of each
+// nibble, and a dword of the operand is one AND of the word with a mask: for G = 0, 1, 2 a set
+// bit reads as the fp4 value 0.5 * 2^G and a clear one as 0, i.e. the operand holds
+// b = (s + 1) / 2 scaled by 0.5 * 2^G; for G = 3 the bit is the fp4 sign and the operand holds
+// s as +-0.5 (one AND and one XOR).  The activation terms of lane group G carry the power of
+// two that makes each product 2 b x' (G < 3) or s x' (G = 3), folded into their block scales,
+// and since s x' = 2 b x' - x', the kernel subtracts, per token, the sum of x' over the columns
+// of groups 0..2, which the prologue leaves per step.  In the fp6 operand field f (bits
+// 6f..6f+5 of six dwords) is position 32G + f; the prologue writes column
+// 32 (f / 8) + 4 (f % 8) + G there, so both operands agree on every product.  The block scale
+// of lane group G covers the 32 columns c = G (mod 4) of the step.
 //
 // Work split.  A workgroup (8 waves, two per SIMD) owns 128 output rows of one linear and up to
 // 256 tokens (16 dense tiles).  The host gives each wave up to ND dense tiles (neighbouring
@@ -78,16 +83,6 @@ __device__ __forceinline__ f32x4 mfma_sign(const u32x4& a, const i32x8& b, int s
                                            const f32x4& c) {
   const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 2, 0, 127, SEL, scale_b);
-}
-
-// The 32 sign bits of one row and one 32-column group -> fp4 +-1.0 in the K order above.
-__device__ __forceinline__ u32x4 expand_fp4(unsigned w) {
-  u32x4 r;
-  r[0] = ((w << 3) & 0x88888888u) ^ 0xAAAAAAAAu;
-  r[1] = ((w << 2) & 0x88888888u) ^ 0xAAAAAAAAu;
-  r[2] = ((w << 1) & 0x88888888u) ^ 0xAAAAAAAAu;
-  r[3] = (w & 0x88888888u) ^ 0xAAAAAAAAu;
-  return r;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -284,7 +279,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 
   // per-lane LDS read offsets
   const unsigned a_lane = (unsigned)j * 256;                      // + stage + rt*4096 + chunk
-  const unsigned s_lane = kWStage + (unsigned)(j * 16 + 4 * g);  // + stage + slot + rt*256
+  const unsigned s_lane = kWStage + (unsigned)j * 16;            // + stage + slot + rt*256
+  // sign operand of lane group g: the bit of column 32 d + 4 n + g as nibble n of dword d; groups
+  // 0..2 keep it as 0.5 * 2^g when set (0 when clear), group 3 as +-0.5
+  const unsigned sm1 = g < 3 ? 0x11111111u << g : 0x88888888u;
+  const unsigned sm2 = g < 3 ? 0u : 0x99999999u;
 
   unsigned st = 0;                                     // stage of step s
   unsigned st_next = (unsigned)ahead * stage_bytes;    // stage of step s + ahead
@@ -294,23 +293,26 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   // its 8 lo-term MFMAs, so dependent MFMAs are 8 apart.  With copies, the wave issues 16 / NG of
   // its copies of step cs before each group.
   u32x4 S[kRT];
+  // Lanes whose token is not of the pair's variant get block scale 2^-127 for both terms, so
+  // their products vanish below fp32 resolution (at most 2^-120 in magnitude per product).
   auto pair_mfma = [&](int i, bool in) {
-    const i32x8 bh = {in ? (int)xq[i][0][0] : 0, in ? (int)xq[i][0][1] : 0,
-                      in ? (int)xq[i][0][2] : 0, in ? (int)xq[i][0][3] : 0,
-                      in ? (int)xq[i][1][0] : 0, in ? (int)xq[i][1][1] : 0, 0, 0};
+    const int sc = in ? (int)xs[i] : 0;
+    const i32x8 bh = {(int)xq[i][0][0], (int)xq[i][0][1], (int)xq[i][0][2], (int)xq[i][0][3],
+                      (int)xq[i][1][0], (int)xq[i][1][1], 0, 0};
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, (int)xs[i], acc[i][rt]);
-    const i32x8 bl = {in ? (int)xq[i][1][2] : 0, in ? (int)xq[i][1][3] : 0,
-                      in ? (int)xq[i][2][0] : 0, in ? (int)xq[i][2][1] : 0,
-                      in ? (int)xq[i][2][2] : 0, in ? (int)xq[i][2][3] : 0, 0, 0};
+    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, sc, acc[i][rt]);
+    const i32x8 bl = {(int)xq[i][1][2], (int)xq[i][1][3], (int)xq[i][2][0], (int)xq[i][2][1],
+                      (int)xq[i][2][2], (int)xq[i][2][3], 0, 0};
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<1>(S[rt], bl, (int)xs[i], acc[i][rt]);
+    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<1>(S[rt], bl, sc, acc[i][rt]);
   };
   auto expand = [&](int slot, unsigned st) {
     const unsigned char* sw = smem + st + s_lane + (unsigned)slot * kSSlot;
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt)
-      S[rt] = expand_fp4(*reinterpret_cast<const unsigned*>(sw + rt * 256));
+    for (int rt = 0; rt < kRT; ++rt) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(sw + rt * 256);
+      S[rt] = u32x4{(w[0] & sm1) ^ sm2, (w[1] & sm1) ^ sm2, (w[2] & sm1) ^ sm2, (w[3] & sm1) ^ sm2};
+    }
   };
   auto sign_phase = [&](bool copies, int cs, unsigned cst, unsigned st) {
 #pragma unroll
@@ -376,6 +378,25 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     if (st == ring) st = 0;
     st_next += stage_bytes;
     if (st_next == ring) st_next = 0;
+  }
+
+  // ---- correction of the unsigned sign columns ----------------------------------------------------
+  // Lane groups 0..2 added 2 b x' for the columns c % 4 < 3 where s x' = 2 b x' - x': subtract the
+  // token's sum of x' over those columns and this piece's steps (lanes 16 g + j of token j add
+  // every fourth step, then combine).
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    if (!dreal[i]) continue;
+    const int tr = 16 * a.wv[wave].tile[i] + j;
+    float cs = 0.f;
+    if (tr >= lo_tok && tr < hi_tok) {
+      const float* xc = P.xc + (size_t)(a.tok_base + tr);
+      for (int s = k0 + g; s < k1; s += 4) cs += xc[(size_t)s * a.Mp];
+    }
+    cs += __shfl_xor(cs, 16);
+    cs += __shfl_xor(cs, 32);
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] -= cs;
   }
 
   // ---- split unit: leave the sums in this piece's slot; the last piece adds all slots ------------
@@ -465,8 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 // A workgroup covers one 16-token block and 4 K steps of one linear, one wave per step; lane
 // L = 16 g + j writes token j's 16-byte slot of every 1 KiB piece of that step (layouts above), so
 // each piece is written whole by one wave.  Every token gets its bf16 pieces; a token of variant
-// v also gets the two fp6 terms of x' = alpha_v * x for its 32-column block g, with their block
-// scales.  Lanes of tokens outside the launch write nothing.
+// v also gets the two fp6 terms of x' = alpha_v * x for the 32 columns c = g (mod 4) of the step,
+// with their block scales, and (lane group 0) the step's correction sum; a base-model token's
+// correction sum is 0.  Lanes of tokens outside the launch write nothing.
 constexpr int kActThreads = 256;
 constexpr int kActSteps = kActThreads / 64;
 
@@ -518,66 +540,84 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
   if (s >= nsteps) return;                   // wave-uniform
   const int tb = (a.tok_base + a.lo) / 16 + (int)(blockIdx.x / nsq);  // absolute 16-token block
   const int t = 16 * tb + j, tr = t - a.tok_base;
-  if (tr < a.lo || tr >= a.hi) return;       // not a token of this launch
+  if (tr < a.lo || tr >= a.hi) return;       // not a token of this launch (all 4 lanes of t)
   const int slot = a.token_slot[tr];
   const size_t nblk = (size_t)a.Mp / 16;
   const size_t ostep = nblk * 1024;          // bytes between consecutive pieces
   const size_t pbase = (size_t)tb * 1024 + (size_t)lane * 16;
   const uint16_t* __restrict__ x = a.x[p] + (size_t)t * d_in + (size_t)s * 128;
 
-  // bf16 pieces (s, c): columns 32c + 8g .. +7 of the step
+  // bf16 pieces (s, c): columns 32c + 8g .. +7 of the step; the four lanes of a token load its
+  // whole 256-byte row of the step, which also goes to LDS (rows padded to 264 bytes, so the
+  // column reads below hit 16 different banks) for the fp6 terms' strided columns
+  __shared__ __attribute__((aligned(16))) uint16_t rows[kActSteps][16][132];
+  uint16_t* row = rows[threadIdx.x >> 6][j];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    *reinterpret_cast<u32x4*>(a.xb[p] + ((size_t)s * 4 + c) * ostep + pbase) =
-        *reinterpret_cast<const u32x4*>(x + 32 * c + 8 * g);
-  if (slot < 0) return;  // base-model token: no sign term
-
-  // fp6 terms of block g: columns 32g .. 32g+31 of the step
-  const float alpha = *a.alpha[p][slot];
-  unsigned v[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x4 c = *reinterpret_cast<const u32x4*>(x + 32 * g + 8 * q);
-    v[4 * q] = c[0];
-    v[4 * q + 1] = c[1];
-    v[4 * q + 2] = c[2];
-    v[4 * q + 3] = c[3];
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + 32 * c + 8 * g);
+    *reinterpret_cast<u32x4*>(a.xb[p] + ((size_t)s * 4 + c) * ostep + pbase) = v;
+    *reinterpret_cast<u32x2*>(row + 32 * c + 8 * g) = u32x2{v[0], v[1]};
+    *reinterpret_cast<u32x2*>(row + 32 * c + 8 * g + 4) = u32x2{v[2], v[3]};
   }
-  float xp[32];  // x' in operand order: field f <- column 4 (f % 8) + f / 8 of the block
+  float* corr = a.xc[p] + (size_t)s * a.Mp + t;
+  if (slot < 0) {  // base-model token: no sign term, no correction
+    if (g == 0) *corr = 0.f;
+    return;
+  }
+  // the row of token j was written by lanes j, j+16, j+32, j+48 of this wave, all still here
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+
+  // fp6 terms of lane group g: the 32 columns c = g (mod 4) of the step, field f <- column
+  // 32 (f / 8) + 4 (f % 8) + g
+  const float alpha = *a.alpha[p][slot];
+  float xp[32];
   float m = 0.f;
 #pragma unroll
   for (int f = 0; f < 32; ++f) {
-    const int col = 4 * (f & 7) + (f >> 3);
-    const unsigned pair = v[col >> 1];
-    xp[f] = alpha * ((col & 1) ? bf16hi_to_f32(pair) : bf16lo_to_f32(pair));
+    const unsigned b = row[32 * (f >> 3) + 4 * (f & 7) + g];
+    xp[f] = alpha * __uint_as_float(b << 16);
     m = fmaxf(m, fabsf(xp[f]));
   }
   int ea = m > 0.f ? e2m3_block_exp(m) : 0;
-  ea = max(-126, min(127, ea));
+  ea = max(-126, min(125, ea));
   const float sa = pow2f(ea), inva = pow2f(-min(ea, 126));
   unsigned hi[6] = {0, 0, 0, 0, 0, 0}, lo[6] = {0, 0, 0, 0, 0, 0};
+  float hv[32];
   float rm = 0.f;
 #pragma unroll
   for (int f = 0; f < 32; ++f) {
-    float hv;
-    put6(hi, f, e2m3_round(xp[f] * inva, &hv));
-    xp[f] -= hv * sa;                        // remainder
+    put6(hi, f, e2m3_round(xp[f] * inva, &hv[f]));
+    hv[f] *= sa;                             // value of the hi term
+    xp[f] -= hv[f];                          // remainder
     rm = fmaxf(rm, fabsf(xp[f]));
   }
   int eb = rm > 0.f ? e2m3_block_exp(rm) : ea;
-  eb = max(-126, min(127, eb));
-  const float invb = pow2f(-min(eb, 126));
+  eb = max(-126, min(125, eb));
+  const float sb = pow2f(eb), invb = pow2f(-min(eb, 126));
+  float cs = 0.f;                            // sum of this lane's quantized x', in field order
 #pragma unroll
   for (int f = 0; f < 32; ++f) {
     float lv;
     put6(lo, f, e2m3_round(xp[f] * invb, &lv));
+    cs += hv[f] + lv * sb;
   }
   unsigned char* q = a.xq[p] + pbase;
   *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 0) * ostep) = u32x4{hi[0], hi[1], hi[2], hi[3]};
   *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 1) * ostep) = u32x4{hi[4], hi[5], lo[0], lo[1]};
   *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 2) * ostep) = u32x4{lo[2], lo[3], lo[4], lo[5]};
+  // Block scales with the lane group's operand factor: the sign operand of lane groups 0..2
+  // holds the bit b = (s + 1) / 2 as 0.5 * 2^g, so their terms carry 2^(2-g) (the products are
+  // 2 b x'); lane group 3 holds s as +-0.5, so its terms carry 2 (the products are s x').
+  const int fe = g < 3 ? 2 - g : 1;
   *reinterpret_cast<unsigned*>(a.xs[p] + ((size_t)s * nblk + tb) * 256 + (size_t)lane * 4) =
-      (unsigned)(ea + 127) | ((unsigned)(eb + 127) << 8);
+      (unsigned)(ea + fe + 127) | ((unsigned)(eb + fe + 127) << 8);
+  // correction: s x' = 2 b x' - x' on lane groups 0..2, so the token's products over this step
+  // need sum(x') of those columns subtracted; lanes 16g + j with g = 0..3 hold token j
+  if (g == 3) cs = 0.f;
+  cs += __shfl_xor(cs, 16);
+  cs += __shfl_xor(cs, 32);
+  if (g == 0) *corr = cs;
 }
 
 // Dynamic LDS one workgroup may use on the current device, capped at one compute unit's.
@@ -615,11 +655,12 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 }  // namespace
 
 void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq_bytes,
-                           size_t* xs_bytes) {
+                           size_t* xs_bytes, size_t* xc_bytes) {
   const size_t mp = (size_t)((M + 15) / 16) * 16;
   *xb_bytes = round256(mp * 2 * (size_t)d_in);       // bf16
   *xq_bytes = round256(mp * 3 * (size_t)d_in / 2);   // two fp6 terms: 12 bits per element
   *xs_bytes = round256(mp * (size_t)d_in / 8);       // 4 bytes per token and 32 columns
+  *xc_bytes = round256(mp * (size_t)d_in / 32);      // 4 bytes per token and 128 columns
 }
 
 size_t split_slot_bytes(int64_t M) {
@@ -632,9 +673,9 @@ size_t split_partial_bytes(int64_t M) {
 }
 
 size_t split_workspace_bytes(int64_t M, int64_t d_in) {
-  size_t b, q, c;
-  split_workspace_parts(M, d_in, &b, &q, &c);
-  return b + q + c + split_partial_bytes(M);
+  size_t b, q, c, k;
+  split_workspace_parts(M, d_in, &b, &q, &c, &k);
+  return b + q + c + k + split_partial_bytes(M);
 }
 
 hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream) {

@@ -185,10 +185,12 @@ def test_matmul_workspace_bytes():
     # (1.5 bytes per element) and one 4-byte scale word per 32 elements, each region rounded
     # up to 256 bytes; then the linear's share of the call's partial slots (128 slots of
     # 128 rows x 4 bytes per token) and of its split counters (128 x 4 bytes)
+    # and one fp32 correction sum per token and 128 columns
     part = lambda mp: 128 * 128 * 4 * mp + 512
     assert bd.matmul_workspace_bytes(256, 8192) == (256 * 8192 * 2 + 256 * 8192 * 3 // 2
-                                                    + 256 * 8192 // 8 + part(256))
-    assert bd.matmul_workspace_bytes(5, 128, "split") == 16 * 128 * 2 + 16 * 128 * 3 // 2 + 256 + part(16)
+                                                    + 256 * 8192 // 8 + 256 * 8192 // 32 + part(256))
+    assert bd.matmul_workspace_bytes(5, 128, "split") == (16 * 128 * 2 + 16 * 128 * 3 // 2 + 256
+                                                          + 256 + part(16))
     assert bd.matmul_workspace_bytes(4, 8192) == 0            # AUTO -> GEMV, no workspace
     assert bd.matmul_workspace_bytes(300, 8192) == 0          # AUTO -> PREFILL
     assert bd.matmul_workspace_bytes(64, 8192, "stream") == 0
