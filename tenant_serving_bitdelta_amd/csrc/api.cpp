@@ -507,9 +507,11 @@ bitdelta_status run_prefill(const bitdelta_problem* probs, int np,
       a.y_f32 = y_f32;
       a.n_mtiles = (int)(m1 - m0);
       a.n_ntiles = (int)((P.d_out + bd::kPrefillBN - 1) / bd::kPrefillBN);
+      a.vec_signs = P.d_in % 128 == 0;
       for (int s = 0; s < (int)slot_var.size(); ++s) {
         a.words[s] = P.variants[slot_var[s]].sign_words;
         a.alpha[s] = P.variants[slot_var[s]].alpha;
+        if (!aligned(a.words[s], 16)) a.vec_signs = 0;
       }
       bitdelta_status r = map_hip(bd::launch_prefill(a, st));
       if (r != BITDELTA_OK) return r;

@@ -85,16 +85,17 @@ struct StreamArgs {
 hipError_t launch_stream(const StreamArgs& a, int nblocks, hipStream_t stream);
 size_t stream_lds_bytes(int ntiles, int nslots);
 
-// Prefill: per-segment tiles of 256 tokens x 128 output rows, W_eff rebuilt in LDS.
+// Prefill: per-segment tiles of 256 tokens x 256 output rows, W_eff rebuilt in LDS.
 constexpr int kPrefillBM = 256;
-constexpr int kPrefillBN = 128;
+constexpr int kPrefillBN = 256;
 constexpr int kPrefillMaxMTiles = 256;
 
 struct PrefillArgs {
   const uint16_t* x;
   const uint16_t* w;
   void* y;
-  int d_out, d_in, y_f32, n_mtiles, n_ntiles, pad_;
+  int d_out, d_in, y_f32, n_mtiles, n_ntiles;
+  int vec_signs;                       // every words[] 16-byte aligned and d_in % 128 == 0
   const uint32_t* words[kMaxSlots];
   const float* alpha[kMaxSlots];
   // per M-tile: first x row, rows in the tile (1..256), variant slot (-1 = base)
