@@ -3,23 +3,20 @@
 // written to HBM) as a dense bf16 MFMA contraction per segment.
 //
 // A workgroup (8 waves, two per SIMD) computes a tile of 256 tokens (one segment, hence one
-// variant) by 256 output rows, walking d_in in steps of 32 grouped in quads of 4 steps.  Wave w
-// owns rows 32w .. 32w + 31 for all 256 tokens:
-//   * its W_base rows (16 bytes per lane: exactly the bf16 MFMA operand of one row tile) and
-//     their sign words (one 16-byte load per row covers the quad) go straight from memory into
-//     registers one quad ahead, and each weight is rebuilt in registers by the wave that
-//     multiplies it,
+// variant) by 256 output rows, walking d_in in steps of 32 taken in pairs.  Wave w owns rows
+// 32w .. 32w + 31 for all 256 tokens.  Per pair of steps:
+//   * the 256x64 block of activations, which every wave needs, and wave w's own 32x64 block of
+//     W_base go straight from memory into LDS (direct global->LDS loads of whole 128-byte lines,
+//     16 bytes per lane, one pair ahead, double-buffered); 16-byte units are XOR-swizzled by row
+//     so the operand reads are conflict-free;
+//   * each wave reads its raw weights back and rebuilds them in registers,
 //         W_eff = bf16(fp32(w) + (bit ? +alpha : -alpha))   (round to nearest even),
-//     so no weight passes through LDS and no other wave waits for it;
-//   * the quad's 256x128 block of activations, which every wave needs, goes straight from
-//     memory into an 8-step LDS ring (direct global->LDS loads, 16 bytes per lane, one quad
-//     ahead, one eighth per wave); 16-byte chunks are XOR-swizzled by token so the operand reads
-//     are conflict-free;
+//     with the sign words (one 16-byte load per row per 4 steps) in registers one quad ahead,
+//     so each weight is rebuilt once, by the wave that multiplies it;
 //   * v_mfma_f32_16x16x32_bf16 over 2 row tiles x 16 token tiles, fp32 accumulation.
-// The next quad's loads are spread over the first steps of the quad, between the MFMAs; one
-// barrier per quad.  Rounding W_eff to bf16 before the product is the one departure from an
-// exact W_eff; the error it adds is below half a bf16 ulp of each weight and shows in y far
-// inside the output tolerance.
+// One barrier per pair (the activations).  Rounding W_eff to bf16 before the product is the one
+// departure from an exact W_eff; the error it adds is below half a bf16 ulp of each weight and
+// shows in y far inside the output tolerance.
 //
 // Tile order: workgroup b runs on XCD b % 8.  Each XCD takes groups of 32 tiles, 4 M tiles by 8
 // N tiles, so the workgroups running side by side on it share 4 activation blocks and 8 weight
@@ -33,10 +30,10 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kBK = 32;                            // K per step
-constexpr int kStages = 8;                         // activation ring
-constexpr int kAhead = kStages - 1;                // copies issued this many steps ahead
-constexpr unsigned kXBytes = kPrefillBM * kBK * 2;  // 16 KiB of activations per stage
-constexpr unsigned kLds = kStages * kXBytes;
+constexpr unsigned kXPair = kPrefillBM * 2 * kBK * 2;   // 32 KiB of activations per pair
+constexpr unsigned kWPair = kPrefillBN * 2 * kBK * 2;   // 32 KiB of W_base per pair
+constexpr unsigned kPair = kXPair + kWPair;
+constexpr unsigned kLds = 2 * kPair;                    // double-buffered
 static_assert(kLds <= 160 * 1024, "the ring must fit in one compute unit's LDS");
 constexpr int kGroupM = 4, kGroupN = 8;            // tiles per XCD group
 
@@ -63,9 +60,11 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned voff, unsigned char* ld
 #define PREFILL_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// Byte offset in a stage of token r's 16-byte chunk c (4 chunks of 8 bf16 per token).
-__device__ __forceinline__ unsigned chunk_off(int r, int c) {
-  return (unsigned)(4 * r + (c ^ ((r >> 2) & 3))) * 16u;
+// Byte offset of row t's 16-byte unit u in a pair block (units 4 h + c: chunk c of step h of the
+// pair, 8 bf16 each): each row's 128 bytes are contiguous, with the units XOR-swizzled by
+// (t / 2) % 8 so that 16 consecutive rows reading the same unit hit 16 different banks.
+__device__ __forceinline__ unsigned unit_off(int t, int u) {
+  return (unsigned)(8 * t + (u ^ ((t >> 1) & 7))) * 16u;
 }
 
 // +alpha where bit `pos` of word is set, -alpha where it is clear (alpha_bits: |alpha|)
@@ -114,56 +113,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
 
-  // ---- activation copies: wave w moves tokens 32w .. 32w + 31 of each step (2 x 1 KiB) --------
+  // ---- copies of a pair: wave w moves tokens 32w .. 32w + 31 (4 x 1 KiB) and its own weight rows
+  // 32w .. 32w + 31 (4 x 1 KiB), 8 rows of 128 bytes per copy: lane L fills stored unit L % 8 of
+  // row 8i + L / 8 of the wave's 32, i.e. unit (L % 8) ^ ((row / 2) % 8) of that row ---------
   const rsrc_t xrs = make_rsrc(a.x + (size_t)xrow0 * d_in);
-  unsigned xoff[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    // block i = 2 wave + u covers tokens 16 i .. 16 i + 15; lane L fills stored chunk L % 4 of
-    // token 16 i + L / 4, i.e. chunk (L % 4) ^ ((token >> 2) & 3) of that token
-    const int tok = 16 * (2 * wave + u) + (lane >> 2);
-    const int c = (lane & 3) ^ ((tok >> 2) & 3);
-    xoff[u] = (unsigned)((min(tok, nrows - 1) * d_in + 8 * c) * 2);
-  }
-  auto copy_x = [&](int s, int u) {  // step s (clamped: past the end it reloads the last step)
-    const int sc = min(s, nsteps - 1);
-    dma16(xrs, xoff[u] + (unsigned)sc * (kBK * 2),
-          smem + (unsigned)(s % kStages) * kXBytes + (2 * wave + u) * 1024);
+  const rsrc_t wrs = make_rsrc(a.w + (size_t)n0 * d_in);
+  auto copy_pair = [&](int p, int i) {  // copy i (0..7) of pair p (past the end: clamped)
+    const int r = 32 * wave + 8 * (i & 3) + (lane >> 3);
+    const int u = (lane & 7) ^ ((r >> 1) & 7);
+    const int sc = min(2 * p + (u >> 2), nsteps - 1);  // the step of this lane's unit
+    unsigned char* dst = smem + (unsigned)(p & 1) * kPair + (unsigned)(32 * wave + 8 * (i & 3)) * 128u;
+    if (i < 4)
+      dma16(xrs, (unsigned)((min(r, nrows - 1) * d_in + sc * kBK + 8 * (u & 3)) * 2), dst);
+    else
+      dma16(wrs, (unsigned)(((min(n0 + r, d_out - 1) - n0) * d_in + sc * kBK + 8 * (u & 3)) * 2),
+            dst + kXPair);
   };
 
-  // ---- weights: lane (j, g) of row tile rt holds row 32w + 16rt + j, columns 8g .. 8g + 7 ------
-  const rsrc_t wrs = make_rsrc(a.w + (size_t)n0 * d_in);
+  // ---- sign words: lane (j, g) of row tile rt holds the 4 words of row 32w + 16rt + j for a quad
   const rsrc_t srs = make_rsrc(slot >= 0 ? static_cast<const void*>(a.words[slot] + (size_t)n0 * wpr)
                                          : static_cast<const void*>(a.w));
-  unsigned woff[2], soff[2];
+  unsigned soff[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = min(n0 + 32 * wave + 16 * rt + j, d_out - 1) - n0;
-    woff[rt] = (unsigned)(r * d_in + 8 * g) * 2u;
-    soff[rt] = (unsigned)(r * wpr) * 4u;
-  }
-  // Registers of one quad: raw weights [step][row tile] and the sign words [row tile] (word t of
-  // the 16-byte load belongs to step t of the quad; with d_in % 128 != 0 the words are loaded one
-  // by one).  Past the last step, loads are clamped to it (in-range data nobody uses).
-  struct Quad {
-    u32x4 w[4][2];
-    u32x4 sw[2];
-  };
+  for (int rt = 0; rt < 2; ++rt)
+    soff[rt] = (unsigned)((min(n0 + 32 * wave + 16 * rt + j, d_out - 1) - n0) * wpr) * 4u;
   const bool vec_signs = a.vec_signs != 0;
-  auto load_w = [&](Quad& Q, int s, int rt) {  // step s of the quad starting at (s & ~3)
-    const int sc = min(s, nsteps - 1);
-    Q.w[s & 3][rt] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, woff[rt] + (unsigned)sc * (kBK * 2), 0, 0));
-  };
-  auto load_s = [&](Quad& Q, int q0, int rt) {  // sign words of the quad starting at step q0
+  auto load_s = [&](u32x4* sw, int q0, int rt) {  // the quad starting at step q0 (clamped)
     if (vec_signs) {
       const int qc = min(q0, (nsteps - 1) & ~3);
-      Q.sw[rt] = __builtin_bit_cast(
+      sw[rt] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, soff[rt] + (unsigned)qc * 4u, 0, 0));
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        Q.sw[rt][t] = __builtin_amdgcn_raw_buffer_load_b32(
+        sw[rt][t] = __builtin_amdgcn_raw_buffer_load_b32(
             srs, soff[rt] + (unsigned)min(q0 + t, nsteps - 1) * 4u, 0, 0);
     }
   };
@@ -174,66 +157,59 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const unsigned b_lane = chunk_off(j, g);  // + tt * 16 tokens * 64 bytes
+  // operand reads: unit 4h + g of token 16 tt + j (B) and of row 32w + 16 rt + j (A)
+  const unsigned b_lane[2] = {unit_off(j, g), unit_off(j, 4 + g)};  // + tt * 16 rows * 128 bytes
+  const unsigned a_lane[2] = {unit_off(32 * wave + j, g) + kXPair,
+                              unit_off(32 * wave + j, 4 + g) + kXPair};  // + rt * 16 * 128
 
-  // One step of a quad: rebuild this step's two weight fragments, multiply by the 16 token tiles
-  // of the stage.
-  auto mma_step = [&](const Quad& Q, int s) {
-    const int t = s & 3;
-    const u32x4 A0 = rebuild8(Q.w[t][0], Q.sw[0][t], 8u * g, abits);
-    const u32x4 A1 = rebuild8(Q.w[t][1], Q.sw[1][t], 8u * g, abits);
-    const unsigned char* st = smem + (unsigned)(s % kStages) * kXBytes + b_lane;
+  // Step s (h = s % 2 of its pair): rebuild the two weight fragments, multiply by the 16 token
+  // tiles.
+  auto mma_step = [&](const u32x4* sw, int s) {
+    const int h = s & 1;
+    const unsigned char* pb = smem + (unsigned)((s >> 1) & 1) * kPair;
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(pb + a_lane[h]);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(pb + a_lane[h] + 16 * 128);
+    const u32x4 A0 = rebuild8(w0, sw[0][s & 3], 8u * g, abits);
+    const u32x4 A1 = rebuild8(w1, sw[1][s & 3], 8u * g, abits);
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
-      const u32x4 B = *reinterpret_cast<const u32x4*>(st + tt * 1024);
+      const u32x4 B = *reinterpret_cast<const u32x4*>(pb + b_lane[h] + tt * 16 * 128);
       acc[0][tt] = mfma(A0, B, acc[0][tt]);
       acc[1][tt] = mfma(A1, B, acc[1][tt]);
     }
   };
-  // A quad: steps q0 .. q0 + 3 from registers cur, while the loads of the next quad (activations
-  // into the other half of the ring, weights and signs into nxt) go out during its first two
-  // steps; all of them must be in before the barrier that ends the quad.
-  auto quad = [&](const Quad& cur, Quad& nxt, int q0) {
-    const int q1 = q0 + 4;
+  // A quad (two pairs): steps q0 .. q0 + 3 with the sign words cur, while the next pair's copies
+  // go out during each pair's first step and the next quad's sign words into nxt; everything a
+  // pair issued is waited for before the barrier that ends it.
+  auto quad = [&](const u32x4* cur, u32x4* nxt, int q0) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < 2) {
-        copy_x(q1 + 2 * t, 0);
-        copy_x(q1 + 2 * t, 1);
-        copy_x(q1 + 2 * t + 1, 0);
-        copy_x(q1 + 2 * t + 1, 1);
-        load_w(nxt, q1 + 2 * t, 0);
-        load_w(nxt, q1 + 2 * t, 1);
-        load_w(nxt, q1 + 2 * t + 1, 0);
-        load_w(nxt, q1 + 2 * t + 1, 1);
-        load_s(nxt, q1, t);
-      }
-      if (q0 + t < nsteps) mma_step(cur, q0 + t);
+    for (int hp = 0; hp < 2; ++hp) {
+      const int p = (q0 >> 1) + hp;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) copy_pair(p + 1, i);
+      load_s(nxt, q0 + 4, hp);
+      if (2 * p < nsteps) mma_step(cur, 2 * p);
+      if (2 * p + 1 < nsteps) mma_step(cur, 2 * p + 1);
+      PREFILL_VMCNT(0);
+      __syncthreads();
     }
-    PREFILL_VMCNT(0);
-    __syncthreads();
   };
 
-  // ---- prologue: the first quad --------------------------------------------------------------
-  Quad qa, qb;
+  // ---- prologue: pair 0 and the sign words of quad 0 -------------------------------------------
+  u32x4 sa[2], sb[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    copy_x(t, 0);
-    copy_x(t, 1);
-    load_w(qa, t, 0);
-    load_w(qa, t, 1);
-  }
-  load_s(qa, 0, 0);
-  load_s(qa, 0, 1);
+  for (int i = 0; i < 8; ++i) copy_pair(0, i);
+  load_s(sa, 0, 0);
+  load_s(sa, 0, 1);
   PREFILL_VMCNT(0);
   __syncthreads();
 
   int q0 = 0;
   for (; q0 + 4 < nsteps; q0 += 8) {
-    quad(qa, qb, q0);
-    quad(qb, qa, q0 + 4);
+    quad(sa, sb, q0);
+    quad(sb, sa, q0 + 4);
   }
-  if (q0 < nsteps) quad(qa, qb, q0);
+  if (q0 < nsteps) quad(sa, sb, q0);
 
   // ---- epilogue: lane holds rows 4g..4g+3 of each row tile for token j of each token tile ----
 #pragma unroll
