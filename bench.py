@@ -58,7 +58,7 @@ def parse():
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                "split_kernel__decode_20x70b_m256_14var__hbm_traffic.md")
 TRAFFIC_SOURCES = [os.path.join(ROOT, "tenant_serving_bitdelta_amd", "csrc", f)
-                   for f in ("split.hip", "bd_internal.h", "api.cpp")]
+                   for f in ("split.hip", "split_sched.cpp", "bd_internal.h", "api.cpp")]
 
 
 def sources_sha256():
