@@ -113,7 +113,8 @@ def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nva
     dev = "cuda"
     maxn = max(d_out * d_in for _, d_out, d_in in linears)
     dbuf = torch.empty(maxn, dtype=torch.float32, device=dev)
-    ws = torch.empty(2048, dtype=torch.float64, device=dev)
+    ws_bytes = max(bd.compress_workspace_bytes(d_out, d_in) for _, d_out, d_in in linears)
+    ws = torch.empty(max(ws_bytes, 8) // 8, dtype=torch.float64, device=dev)
     layers = []
     for b in range(blocks):
         blk = []

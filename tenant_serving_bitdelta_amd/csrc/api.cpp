@@ -556,7 +556,7 @@ int64_t bitdelta_sign_words_t128(int64_t d_out, int64_t d_in) {
 
 size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in) {
   if (d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || d_out >= kMaxDim || d_in >= kMaxDim) return 0;
-  return (size_t)bd::compress_grid(d_out * d_in) * sizeof(double);
+  return (size_t)bd::compress_partials(d_out, d_in) * sizeof(double);
 }
 
 bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
@@ -571,7 +571,7 @@ bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_i
       !aligned(workspace, 8) || !aligned(sign_words_t128, 16))
     return BITDELTA_ERR_ALIGNMENT;
   if (workspace_bytes < bitdelta_compress_workspace_bytes(d_out, d_in)) return BITDELTA_ERR_WORKSPACE;
-  return map_hip(bd::launch_compress(delta, d_out * d_in, d_in, sign_words, sign_words_t128, alpha,
+  return map_hip(bd::launch_compress(delta, d_out, d_in, sign_words, sign_words_t128, alpha,
                                      static_cast<double*>(workspace),
                                      static_cast<hipStream_t>(stream)));
 }

@@ -33,10 +33,12 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
 // ---------------------------------------------------------------------------------------------
 // Compress (two passes)
 // ---------------------------------------------------------------------------------------------
-int compress_grid(int64_t n);  // number of pass-1 workgroups (= fp64 partials) for n elements
+// fp64 partials (workspace doubles) pass 1 may write for a d_out x d_in matrix, whichever of
+// its two forms runs
+int64_t compress_partials(int64_t d_out, int64_t d_in);
 // words: row-major [d_out][d_in/32]; tiled: optional copy in the 128-row tiled layout (NULL for
 // none; needs d_in % 128 == 0).
-hipError_t launch_compress(const float* delta, int64_t n, int64_t d_in, uint32_t* words,
+hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
                            uint32_t* tiled, float* alpha, double* partials, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------

@@ -4,12 +4,21 @@
 //   words (bit 1 = +1), the byte image of the post's eight-bits-per-int8 storage format
 //   ("Infrastructure details").
 //
-// Pass 1 streams Delta once with 16-byte loads.  A wave covers 256 consecutive elements per
-// iteration: lane l holds elements 4l..4l+3, so the 32 elements of one output word live in the
-// 8 lanes 8w..8w+7; their 4-bit groups are OR-combined across those lanes and one lane stores
-// the word.  |Delta| is accumulated in fp64 per lane and reduced per workgroup into one fp64
-// partial.  Pass 2 sums the partials in a fixed order and rounds sum/n once to float32, so the
-// result is identical from run to run (no atomics anywhere).
+// Pass 1 streams Delta once with 16-byte loads; a lane holds 4 consecutive elements, so the 32
+// elements of one output word live in 8 neighbouring lanes, whose 4-bit groups are OR-combined
+// with three shuffles.  Two forms:
+//  * row tiles (d_in a multiple of 128, word arrays 16-byte aligned): a workgroup of 8 waves
+//    takes 8 rows x 1024 columns (32 KiB of Delta), one row per wave.  The 256 words of a tile
+//    are gathered in LDS and written as whole 128-byte lines: one line per row of the plain
+//    words, and, for the tiled copy below, one line per 4-word column group holding the tile's
+//    8 rows.  Scattered 4-byte word stores interleave many small writes with the read stream,
+//    which costs HBM far more than their byte count.
+//  * flat (any d_in that is a multiple of 32): a grid-stride sweep in which one lane of each
+//    8 stores the word (and its tiled copy) directly.
+// |Delta| is accumulated in fp64 per lane (each lane's 4 elements are first added in fp32, a
+// relative error below 2^-23 of that group) and reduced per workgroup into one fp64 partial.
+// Pass 2 sums the partials in a fixed order and rounds sum/n once to float32, so the result is
+// identical from run to run (no atomics anywhere).
 //
 // Optionally pass 1 also writes a second copy of the sign words in the tiled layout the
 // split-activation decode kernel streams: for every block of 128 rows and every 128-column step,
@@ -17,15 +26,21 @@
 //   tiled word ((r / 128) * (d_in / 128) + c / 4) * 512 + (r % 128) * 4 + c % 4  <-  word (r, c),
 // so a block's sign words for one step are read as whole cache lines.  Rows past d_out in the
 // last block are not written.
+#include <algorithm>
+
 #include "bd_internal.h"
 
 namespace bd {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;        // float4 loads in flight per lane
-constexpr int kMaxGrid = 2048;    // workgroups (= partials) at most
+constexpr int kThreads = 256;        // flat pass 1 and pass 2
+constexpr int kUnroll = 4;           // flat: float4 loads in flight per lane
+constexpr int kMaxGrid = 2048;       // flat: workgroups (= partials) at most
+constexpr int kTileWaves = 8;        // row tiles: one row per wave
+constexpr int kTileCols = 1024;      // row tiles: columns per tile (4 float4 loads per lane)
+constexpr int kMaxTileGrid = 16384;  // row tiles: workgroups (= partials) at most
+constexpr int kPass2Threads = 1024;
 
 // 1 if v is strictly negative (negative zero is not); works on the bit pattern so negative
 // subnormals count as negative whatever the denormal mode.
@@ -45,6 +60,9 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Flat form.  kSmall: fewer than 2^32 words, so word indices and their row / column split fit
+// 32-bit math.
+template <bool kSmall>
 __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restrict__ delta,
                                                           int64_t n4,
                                                           uint32_t* __restrict__ words,
@@ -70,10 +88,7 @@ __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restri
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = base + (int64_t)u * stride + lane;
-      acc += fabs((double)v[u][0]);
-      acc += fabs((double)v[u][1]);
-      acc += fabs((double)v[u][2]);
-      acc += fabs((double)v[u][3]);
+      acc += (double)((fabsf(v[u][0]) + fabsf(v[u][1])) + (fabsf(v[u][2]) + fabsf(v[u][3])));
       unsigned part = nonneg_nibble(v[u]) << shift;
       part |= __shfl_xor(part, 1);
       part |= __shfl_xor(part, 2);
@@ -83,8 +98,14 @@ __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restri
         const int64_t w = i >> 3;
         words[w] = part;
         if (tiled) {
-          const int64_t r = w / wpr, c = w - r * wpr;
-          tiled[((r >> 7) * (wpr >> 2) + (c >> 2)) * 512 + (r & 127) * 4 + (c & 3)] = part;
+          if (kSmall) {
+            const unsigned w32 = (unsigned)w, wpr32 = (unsigned)wpr;
+            const unsigned r = w32 / wpr32, c = w32 - r * wpr32;
+            tiled[((size_t)(r >> 7) * (wpr32 >> 2) + (c >> 2)) * 512 + (r & 127) * 4 + (c & 3)] = part;
+          } else {
+            const int64_t r = w / wpr, c = w - r * wpr;
+            tiled[((r >> 7) * (wpr >> 2) + (c >> 2)) * 512 + (r & 127) * 4 + (c & 3)] = part;
+          }
         }
       }
     }
@@ -102,25 +123,92 @@ __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restri
   }
 }
 
-__global__ __launch_bounds__(kThreads) void compress_pass2(const double* __restrict__ partials,
-                                                          int nparts, double n,
-                                                          float* __restrict__ alpha) {
+// Row-tile form.  Tile t covers rows 8 (t / ncg) .. +7 and columns 1024 (t % ncg) .. +1023
+// (ncg = ceil(d_in / 1024)); rows past d_out and columns past d_in are skipped.  wpr = d_in / 32
+// is a multiple of 4, so a 4-word group is wholly inside or outside the row.
+__global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
+    const float* __restrict__ delta, int64_t d_out, int64_t d_in, uint32_t* __restrict__ words,
+    uint32_t* __restrict__ tiled, double* __restrict__ partials) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t wpr = d_in >> 5;
+  const int64_t ncg = (d_in + kTileCols - 1) / kTileCols;
+  const int64_t ntiles = (d_out + kTileWaves - 1) / kTileWaves * ncg;
+  const unsigned shift = 4u * (unsigned)(lane & 7);
+  // sign words of the tile: [row][32 words], two buffers so one barrier per tile suffices
+  __shared__ __align__(16) uint32_t tw[2][kTileWaves][kTileCols / 32];
+  double acc = 0.0;
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x, buf ^= 1) {
+    const int64_t rg = t / ncg, cg = t - rg * ncg;
+    const int64_t r = rg * kTileWaves + wave;
+    f32x4 v[kTileCols / 256];
+#pragma unroll
+    for (int u = 0; u < kTileCols / 256; ++u) {
+      const int64_t c = cg * kTileCols + u * 256 + lane * 4;
+      v[u] = (r < d_out && c < d_in)
+                 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(delta + r * d_in + c))
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kTileCols / 256; ++u) {
+      acc += (double)((fabsf(v[u][0]) + fabsf(v[u][1])) + (fabsf(v[u][2]) + fabsf(v[u][3])));
+      unsigned part = nonneg_nibble(v[u]) << shift;
+      part |= __shfl_xor(part, 1);
+      part |= __shfl_xor(part, 2);
+      part |= __shfl_xor(part, 4);
+      if ((lane & 7) == 0) tw[buf][wave][u * 8 + (lane >> 3)] = part;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // plain words: lane = (row, 4-word group); the 8 lanes of a row fill its 128-byte line
+      const int row = lane >> 3, q = lane & 7;
+      const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
+      if (rr < d_out && wc < wpr)
+        *reinterpret_cast<u32x4*>(words + rr * wpr + wc) =
+            *reinterpret_cast<const u32x4*>(&tw[buf][row][q * 4]);
+    } else if (wave == kTileWaves - 1 && tiled) {
+      // tiled copy: lane = (4-word group, row); the tile's 8 rows of a group are one line
+      const int q = lane >> 3, row = lane & 7;
+      const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
+      if (rr < d_out && wc < wpr)
+        *reinterpret_cast<u32x4*>(tiled + ((rr >> 7) * (wpr >> 2) + (wc >> 2)) * 512 +
+                                  (rr & 127) * 4) =
+            *reinterpret_cast<const u32x4*>(&tw[buf][row][q * 4]);
+    }
+  }
+
+  __shared__ double wsum[kTileWaves];
+  acc = wave_sum(acc);
+  if (lane == 0) wsum[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kTileWaves; ++w) sum += wsum[w];
+    partials[blockIdx.x] = sum;
+  }
+}
+
+__global__ __launch_bounds__(kPass2Threads) void compress_pass2(const double* __restrict__ partials,
+                                                               int nparts, double n,
+                                                               float* __restrict__ alpha) {
   double s = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) s += partials[i];
-  __shared__ double red[kThreads];
+#pragma unroll 4
+  for (int i = threadIdx.x; i < nparts; i += kPass2Threads) s += partials[i];
+  __shared__ double red[kPass2Threads];
   red[threadIdx.x] = s;
   __syncthreads();
 #pragma unroll
-  for (int width = kThreads / 2; width >= 1; width >>= 1) {
+  for (int width = kPass2Threads / 2; width >= 1; width >>= 1) {
     if ((int)threadIdx.x < width) red[threadIdx.x] += red[threadIdx.x + width];
     __syncthreads();
   }
   if (threadIdx.x == 0) alpha[0] = (float)(red[0] / n);
 }
 
-}  // namespace
-
-int compress_grid(int64_t n) {
+int flat_grid(int64_t n) {
   const int64_t n4 = n / 4;
   const int64_t per_block = (int64_t)kThreads * kUnroll;  // float4 per workgroup per sweep
   int64_t g = (n4 + per_block - 1) / per_block;
@@ -129,16 +217,39 @@ int compress_grid(int64_t n) {
   return (int)g;
 }
 
-hipError_t launch_compress(const float* delta, int64_t n, int64_t d_in, uint32_t* words,
+int tile_grid(int64_t d_out, int64_t d_in) {
+  const int64_t ntiles = (d_out + kTileWaves - 1) / kTileWaves * ((d_in + kTileCols - 1) / kTileCols);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, kMaxTileGrid));
+}
+
+}  // namespace
+
+int64_t compress_partials(int64_t d_out, int64_t d_in) {
+  int64_t g = flat_grid(d_out * d_in);
+  if (d_in % 128 == 0) g = std::max<int64_t>(g, tile_grid(d_out, d_in));
+  return g;
+}
+
+hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
                            uint32_t* tiled, float* alpha, double* partials, hipStream_t stream) {
-  const int grid = compress_grid(n);
+  const int64_t n = d_out * d_in;
+  const bool tiles = d_in % 128 == 0 && reinterpret_cast<uintptr_t>(words) % 16 == 0;
+  const int grid = tiles ? tile_grid(d_out, d_in) : flat_grid(n);
   clear_stale_error();
-  hipLaunchKernelGGL(compress_pass1, dim3(grid), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const f32x4*>(delta), n / 4, words, tiled, d_in / 32,
-                     partials);
+  if (tiles)
+    hipLaunchKernelGGL(compress_tiles, dim3(grid), dim3(kTileWaves * 64), 0, stream, delta, d_out,
+                       d_in, words, tiled, partials);
+  else if (n / 32 < (int64_t(1) << 32))
+    hipLaunchKernelGGL(compress_pass1<true>, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const f32x4*>(delta), n / 4, words, tiled, d_in / 32,
+                       partials);
+  else
+    hipLaunchKernelGGL(compress_pass1<false>, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const f32x4*>(delta), n / 4, words, tiled, d_in / 32,
+                       partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compress_pass2, dim3(1), dim3(kThreads), 0, stream, partials, grid,
+  hipLaunchKernelGGL(compress_pass2, dim3(1), dim3(kPass2Threads), 0, stream, partials, grid,
                      (double)n, alpha);
   return hipGetLastError();
 }

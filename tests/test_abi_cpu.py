@@ -55,7 +55,7 @@ def test_sign_words_and_workspace():
     assert bd.sign_words(4096, 4096) * 4 == 4096 * 512
     assert bd.compress_workspace_bytes(256, 512) >= 8
     assert bd.compress_workspace_bytes(8192, 28672) % 8 == 0
-    assert bd.compress_workspace_bytes(8192, 28672) <= 2048 * 8
+    assert bd.compress_workspace_bytes(8192, 28672) <= 16384 * 8
     assert bd.compress_workspace_bytes(10, 31) == 0
 
 

@@ -52,13 +52,36 @@ def test_compress_config1():
     check_compress(WL.config1()["deltas"][0])
 
 
+# d_in % 128 == 0 runs the row-tile form (8 rows x 1024 columns per workgroup; ragged rows,
+# a narrow last column group); other d_in run the flat form
 @pytest.mark.parametrize("d_out,d_in,seed", [(1, 32, 1), (3, 64, 2), (17, 96, 3), (64, 1056, 4),
-                                             (255, 512, 5), (1000, 4096, 6), (33, 8192, 7)])
+                                             (255, 512, 5), (1000, 4096, 6), (33, 8192, 7),
+                                             (9, 1152, 8), (130, 3200, 9), (1, 128, 10)])
 def test_compress_shapes(d_out, d_in, seed):
     rng = np.random.default_rng(seed)
     d = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
     d[rng.random(d.shape) < 0.02] = 0.0
     check_compress(d)
+
+
+def test_compress_flat_form_unaligned_words():
+    # word array only 4-byte aligned: the flat form writes words and the tiled copy itself
+    rng = np.random.default_rng(12)
+    d_out, d_in = 77, 2048
+    d = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
+    buf = torch.empty(d_out * d_in // 32 + 4, dtype=torch.int32, device="cuda")
+    words = buf[1:1 + d_out * d_in // 32].view(d_out, d_in // 32)
+    assert words.data_ptr() % 16 != 0
+    alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+    tiled = torch.empty(bd.sign_words_t128(d_out, d_in), dtype=torch.int32, device="cuda")
+    bd.compress(f32_dev(d), words, alpha, tiled=tiled)
+    torch.cuda.synchronize()
+    ref_words, ref_alpha = O.compress_ref(d)
+    np.testing.assert_array_equal(words_host(words), ref_words)
+    assert abs(float(alpha.cpu()[0]) - float(ref_alpha)) <= 1e-6 * float(ref_alpha)
+    real = tile_words_128(np.ones_like(ref_words), d_out, d_in) == 1
+    got = tiled.cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(got[real], tile_words_128(ref_words, d_out, d_in)[real])
 
 
 def test_compress_special_values():
