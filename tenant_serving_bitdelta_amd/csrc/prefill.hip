@@ -7,10 +7,12 @@
 // 32w .. 32w + 31 for all 256 tokens.  Per pair of steps:
 //   * the 256x64 block of activations, which every wave needs, and wave w's own 32x64 block of
 //     W_base go straight from memory into LDS (direct global->LDS loads of whole 128-byte lines,
-//     16 bytes per lane, one pair ahead, double-buffered); 16-byte units are XOR-swizzled by row
-//     so the operand reads are conflict-free;
+//     16 bytes per lane, one pair ahead, double-buffered, issued between the matrix
+//     instructions of the pair's first step); 16-byte units are XOR-swizzled by row so the
+//     operand reads are conflict-free;
 //   * each wave reads its raw weights back and rebuilds them in registers,
 //         W_eff = bf16(fp32(w) + (bit ? +alpha : -alpha))   (round to nearest even),
+//     one bf16 dot-product instruction per weight for the widening and the add,
 //     with the sign words (one 16-byte load per row per 4 steps) in registers one quad ahead,
 //     so each weight is rebuilt once, by the wave that multiplies it;
 //   * v_mfma_f32_16x16x32_bf16 over 2 row tiles x 16 token tiles, fp32 accumulation.
@@ -67,20 +69,33 @@ __device__ __forceinline__ unsigned unit_off(int t, int u) {
   return (unsigned)(8 * t + (u ^ ((t >> 1) & 7))) * 16u;
 }
 
-// +alpha where bit `pos` of word is set, -alpha where it is clear (alpha_bits: |alpha|)
-__device__ __forceinline__ float signed_alpha(unsigned alpha_bits, unsigned word, unsigned pos) {
-  return __uint_as_float(alpha_bits | ((~(word << (31u - pos))) & 0x80000000u));
+// bit 31 of s, bits 0..30 of m (one v_bfi_b32)
+__device__ __forceinline__ unsigned sign_into(unsigned s, unsigned m) {
+  unsigned r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(0x80000000u), "v"(s), "v"(m));
+  return r;
 }
 
-// 8 bf16 weights (k = pos0 .. pos0+7 of word) -> 8 bf16 of w + (+-alpha)
-__device__ __forceinline__ u32x4 rebuild8(const u32x4& w, unsigned word, unsigned pos0,
-                                          unsigned abits) {
+// 8 bf16 weights (k = pos0 .. pos0+7 of word) -> 8 bf16 of w + (+-alpha).  The widening of each
+// weight and the add are one bf16 dot product with one_lo = (1, 0) or one_hi = (0, 1) that
+// accumulates onto +-alpha: w * 1 is exact, so the result is fp32(w + (+-alpha)) rounded once.
+// nword = ~word: bit k clear gives the sign bit of -alpha.  one_lo and one_hi must come in
+// registers: encoded in the instruction as a constant, (1, 0) and (0, 1) are not read as these
+// bf16 pairs.
+__device__ __forceinline__ u32x4 rebuild8(const u32x4& w, unsigned nword, unsigned pos0,
+                                          unsigned abits, bf16x2 one_lo, bf16x2 one_hi) {
   u32x4 r;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
+    // through a scalar: a bit cast of the vector element itself reads element 0
+    const unsigned wd = w[d];
+    const bf16x2 wp = __builtin_bit_cast(bf16x2, wd);
+    const unsigned k0 = pos0 + 2 * d;
+    const float a0 = __uint_as_float(sign_into(nword << (31u - k0), abits));
+    const float a1 = __uint_as_float(sign_into(nword << (30u - k0), abits));
     f32x2 f;
-    f[0] = bf16lo_to_f32(w[d]) + signed_alpha(abits, word, pos0 + 2 * d);
-    f[1] = bf16hi_to_f32(w[d]) + signed_alpha(abits, word, pos0 + 2 * d + 1);
+    f[0] = __builtin_amdgcn_fdot2_f32_bf16(wp, one_lo, a0, false);
+    f[1] = __builtin_amdgcn_fdot2_f32_bf16(wp, one_hi, a1, false);
     r[d] = __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
   }
   return r;
@@ -162,34 +177,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   const unsigned a_lane[2] = {unit_off(32 * wave + j, g) + kXPair,
                               unit_off(32 * wave + j, 4 + g) + kXPair};  // + rt * 16 * 128
 
+  // the bf16 pairs (1, 0) and (0, 1) of the rebuild, kept in registers the compiler cannot fold
+  unsigned one_bits[2] = {0x00003F80u, 0x3F800000u};
+  asm volatile("" : "+v"(one_bits[0]), "+v"(one_bits[1]));
+  const bf16x2 one_lo = __builtin_bit_cast(bf16x2, one_bits[0]);
+  const bf16x2 one_hi = __builtin_bit_cast(bf16x2, one_bits[1]);
+
   // Step s (h = s % 2 of its pair): rebuild the two weight fragments, multiply by the 16 token
   // tiles.
-  auto mma_step = [&](const u32x4* sw, int s) {
+  // With cp >= 0 the wave also issues its 8 copies of pair cp, one after every second token
+  // tile: spread between the matrix instructions they keep the memory queue from filling up
+  // and stalling the wave's issue.
+  auto mma_step = [&](const u32x4* sw, int s, int cp) {
     const int h = s & 1;
     const unsigned char* pb = smem + (unsigned)((s >> 1) & 1) * kPair;
     const u32x4 w0 = *reinterpret_cast<const u32x4*>(pb + a_lane[h]);
     const u32x4 w1 = *reinterpret_cast<const u32x4*>(pb + a_lane[h] + 16 * 128);
-    const u32x4 A0 = rebuild8(w0, sw[0][s & 3], 8u * g, abits);
-    const u32x4 A1 = rebuild8(w1, sw[1][s & 3], 8u * g, abits);
+    const u32x4 A0 = rebuild8(w0, ~sw[0][s & 3], 8u * g, abits, one_lo, one_hi);
+    const u32x4 A1 = rebuild8(w1, ~sw[1][s & 3], 8u * g, abits, one_lo, one_hi);
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       const u32x4 B = *reinterpret_cast<const u32x4*>(pb + b_lane[h] + tt * 16 * 128);
       acc[0][tt] = mfma(A0, B, acc[0][tt]);
       acc[1][tt] = mfma(A1, B, acc[1][tt]);
+      if (cp >= 0 && (tt & 1) == 1) copy_pair(cp, tt >> 1);
     }
   };
   // A quad (two pairs): steps q0 .. q0 + 3 with the sign words cur, while the next pair's copies
-  // go out during each pair's first step and the next quad's sign words into nxt; everything a
-  // pair issued is waited for before the barrier that ends it.
+  // go out between the matrix instructions of each pair's first step and the next quad's sign
+  // words into nxt; everything a pair issued is waited for before the barrier that ends it.
   auto quad = [&](const u32x4* cur, u32x4* nxt, int q0) {
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
       const int p = (q0 >> 1) + hp;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) copy_pair(p + 1, i);
       load_s(nxt, q0 + 4, hp);
-      if (2 * p < nsteps) mma_step(cur, 2 * p);
-      if (2 * p + 1 < nsteps) mma_step(cur, 2 * p + 1);
+      if (2 * p < nsteps) {
+        mma_step(cur, 2 * p, p + 1);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) copy_pair(p + 1, i);
+      }
+      if (2 * p + 1 < nsteps) mma_step(cur, 2 * p + 1, -1);
       PREFILL_VMCNT(0);
       __syncthreads();
     }
