@@ -81,3 +81,98 @@ def test_full_size_block_sampled(config, m, dist):
                 err = np.linalg.norm(got - ref, axis=1)
                 assert (err / np.linalg.norm(ref, axis=1)).max() <= row_tol, (name, v)
                 assert (err / np.linalg.norm(delta_term, axis=1)).max() <= res_tol, (name, v)
+
+
+def _check_rows(got, ref, delta_term, row_tol, res_tol, what):
+    err = np.linalg.norm(got - ref, axis=1)
+    rel = err / np.linalg.norm(ref, axis=1)
+    res = err / np.linalg.norm(delta_term, axis=1)
+    assert rel.max() <= row_tol, (what, "row rel L2", float(rel.max()))
+    assert res.max() <= res_tol, (what, "delta residual", float(res.max()))
+
+
+def test_full_size_gemv_one_token():
+    """One token through the 8192 x 28672 down projection with one variant (the GEMV path, as
+    bench.py --config 2 times it): 256 sampled output rows against the oracle, alpha over the
+    whole Delta."""
+    config, name, d_out, d_in = 2, "down", 8192, 28672
+    rng = np.random.default_rng(1002)
+    w = WL.gpu_normal_bf16(torch, (d_out, d_in), 0.02, WL.substream_seed(config, 0, name, "w"))
+    d = WL.gpu_laplace_f32(torch, (d_out, d_in), 2e-4, WL.substream_seed(config, 0, name, 0, "delta"))
+    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+    bd.compress(d, words, alpha)
+    ids = WL.decode_token_ids(config, 1, 1, "uniform")
+    perm, offs, segv = bd.plan_segments(ids, 1)
+    x = WL.gpu_normal_bf16(torch, (1, d_in), 1.0, WL.substream_seed(config, 0, name, "x"))
+    assert bd.auto_path(1, offs, segv) == bd.PATHS["gemv"]
+    y16 = bd.matmul(x, w, [(words, alpha)], offs, segv)
+    y32 = bd.matmul(x, w, [(words, alpha)], offs, segv, out_dtype="f32")
+    torch.cuda.synchronize()
+
+    dh = d.cpu().numpy()
+    del d
+    a_ref = O.alpha_ref(dh)
+    assert abs(float(alpha.item()) - float(a_ref)) <= 1e-6 * abs(float(a_ref))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, d_out - 2, d_out - 1],
+                                     rng.choice(d_out, size=250, replace=False)]))
+    s_rows = O.signs_ref(dh[rows]).astype(np.float64)
+    np.testing.assert_array_equal(words[rows].cpu().numpy().view(np.uint32),
+                                  O.pack_signs_ref(O.signs_ref(dh[rows])))
+    wf = w[rows].float().cpu().numpy().astype(np.float64)
+    xf = x.float().cpu().numpy().astype(np.float64)
+    ref = xf @ (wf + np.float64(a_ref) * s_rows).T
+    delta_term = np.float64(a_ref) * (xf @ s_rows.T)
+    # the sampled outputs of the one token form its "row" here
+    _check_rows(y16.float().cpu().numpy().astype(np.float64)[:, rows], ref, delta_term, 2e-2, 0.75,
+                "bf16")
+    _check_rows(y32.cpu().numpy().astype(np.float64)[:, rows], ref, delta_term, 1e-5, 1e-2, "f32")
+
+
+def test_full_size_prefill_sampled():
+    """The gate projection (28672 x 8192) over 4 requests x 2048 tokens on 4 of 14 resident
+    variants, on the prefill path as bench.py --config 4 times it: 8 tokens of every segment on
+    24 sampled output rows against the oracle."""
+    config, name, d_out, d_in, nvar = 4, "gate", 28672, 8192, 14
+    rng = np.random.default_rng(1004)
+    scales = WL.decode_variant_scales(config)
+    req_var = WL.prefill_request_variants(config, 4, nvar)
+    ids = np.repeat(req_var, 2048).astype(np.int32)
+    perm, offs, segv = bd.plan_segments(ids, nvar)
+    m = ids.size
+    w = WL.gpu_normal_bf16(torch, (d_out, d_in), 0.02, WL.substream_seed(config, 0, name, "w"))
+    x = WL.gpu_normal_bf16(torch, (m, d_in), 1.0, WL.substream_seed(config, 0, name, "x"))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, d_out - 2, d_out - 1],
+                                     rng.choice(d_out, size=18, replace=False)]))
+    variants, checked = [], {}
+    for v in range(nvar):
+        d = WL.gpu_laplace_f32(torch, (d_out, d_in), scales[v], WL.substream_seed(config, 0, name, v, "delta"))
+        words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+        alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+        bd.compress(d, words, alpha)
+        variants.append((words, alpha))
+        if v in set(int(r) for r in req_var):
+            dh = d.cpu().numpy()
+            a_ref = O.alpha_ref(dh)
+            assert abs(float(alpha.item()) - float(a_ref)) <= 1e-6 * abs(float(a_ref)), v
+            checked[v] = (a_ref, O.signs_ref(dh[rows]).astype(np.float64))
+            del dh
+        del d
+    y16 = torch.empty((m, d_out), dtype=torch.bfloat16, device="cuda")
+    y32 = torch.empty((m, d_out), dtype=torch.float32, device="cuda")
+    bd.matmul_grouped([(x, w, y16, variants)], offs, segv, path="prefill")
+    bd.matmul_grouped([(x, w, y32, variants)], offs, segv, path="prefill", out_dtype="f32")
+    torch.cuda.synchronize()
+
+    wf = w[rows].float().cpu().numpy().astype(np.float64)
+    for sgi, v in enumerate(segv):
+        lo, hi = int(offs[sgi]), int(offs[sgi + 1])
+        toks = np.unique(np.concatenate([[lo, lo + 1, hi - 2, hi - 1], rng.integers(lo, hi, size=4)]))
+        a_ref, s_rows = checked[int(v)]
+        xf = x[toks].float().cpu().numpy().astype(np.float64)
+        ref = xf @ (wf + np.float64(a_ref) * s_rows).T
+        delta_term = np.float64(a_ref) * (xf @ s_rows.T)
+        got16 = y16[toks][:, rows].float().cpu().numpy().astype(np.float64)
+        got32 = y32[toks][:, rows].cpu().numpy().astype(np.float64)
+        _check_rows(got16, ref, delta_term, 2e-2, 0.75, ("bf16", int(v)))
+        _check_rows(got32, ref, delta_term, 5e-3, 0.75, ("f32", int(v)))
