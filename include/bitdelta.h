@@ -118,12 +118,15 @@ size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
  * elements (exact zeros included), and sign(Delta) packed one bit per element.
  *
  *   delta       [dev] float32 [d_out][d_in], 16-byte aligned, finite values.  Read only.
- *   sign_words  [dev] out: uint32 [d_out][d_in/32] (layout above), 4-byte aligned.
+ *   sign_words  [dev] out: uint32 [d_out][d_in/32] (layout above), 4-byte aligned; with
+ *               d_in % 128 == 0 and 16-byte alignment the words are written as whole lines
+ *               (the faster form), otherwise word by word.
  *   sign_words_t128 [dev] out, optional (NULL = not written): the same bits in the tiled
  *               layout above, bitdelta_sign_words_t128 words, 16-byte aligned; needs
  *               d_in % 128 == 0 (else SHAPE).
- *   alpha       [dev] out: one float32, the fp64 sum of |Delta| (fixed summation order, so
- *               repeated calls are bit-identical) divided by n and rounded once to float32.
+ *   alpha       [dev] out: one float32, the sum of |Delta| (each 4 consecutive elements added
+ *               in fp32, those sums in fp64, in a fixed order, so repeated calls are
+ *               bit-identical) divided by n and rounded once to float32.
  *   workspace   [dev] at least bitdelta_compress_workspace_bytes(d_out, d_in) bytes,
  *               8-byte aligned; scratch only, contents on return unspecified.
  * Errors: INVALID_ARG (null pointer, d_out <= 0), SHAPE (d_in not a positive multiple of 32),
