@@ -505,29 +505,29 @@ __device__ __forceinline__ int e2m3_block_exp(float m) {
   return (b & 0x7FFFFFu) <= 0x700000u ? E - 2 : E - 1;
 }
 
-// e2m3 code of v (|v| <= 7.5) rounded to nearest even, and the value of that code.  In the
-// binade [2^e, 2^(e+1)), e = 0, 1, 2, the grid spacing is 2^(e-3) (and 1/8 below 1, the
-// subnormals): the nearest grid point is n 2^(e-3) with n = rint(|v| 2^(3-e)) in [0, 16], and
-// its code is n + 8e (n = 16 is the first point of the next binade, whose code is 8 (e+1) + 8).
-__device__ __forceinline__ unsigned e2m3_round(float v, float* value) {
-  const float a = fabsf(v);
-  const int e = max((int)(__float_as_uint(a) >> 23) - 127, 0);
-  const float n = rintf(a * __uint_as_float((unsigned)(130 - e) << 23));  // exact scaling
-  const float r = n * __uint_as_float((unsigned)(124 + e) << 23);
-  const unsigned c = (unsigned)n + 8u * (unsigned)e;
-  *value = v < 0.f ? -r : r;
-  return (v < 0.f && r != 0.f) ? (c | 32u) : c;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+
+// 32 values / scale as e2m3 codes, rounded to nearest even (saturating at 7.5): field 2i of the
+// six dwords takes even[i], field 2i + 1 takes odd[i].  Written out rather than through the
+// compiler's builtin: with the builtin the compiler gave the destination registers that overlap
+// the last source registers, and the instruction then converted overwritten inputs (wrong codes
+// in the last odd fields, seen on the GPU); an early-clobber output keeps them apart.
+__device__ __forceinline__ i32x6 cvt_e2m3x32(const f32x16& even, const f32x16& odd, float scale) {
+  i32x6 r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(even), "v"(odd), "v"(scale));
+  return r;
+}
+// the 32 values of six dwords of e2m3 codes (field f -> element f), times scale
+__device__ __forceinline__ f32x32 e2m3x32_values(const i32x6& codes, float scale) {
+  f32x32 r;
+  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(r) : "v"(codes), "v"(scale));
+  return r;
 }
 
 __device__ __forceinline__ float pow2f(int e) {  // 2^e for -126 <= e <= 127
   return __uint_as_float((unsigned)(e + 127) << 23);
-}
-
-// fp6 field f (6 bits) into a 6-dword little-endian field array
-__device__ __forceinline__ void put6(unsigned* w, int f, unsigned c) {
-  const int bit = 6 * f;
-  w[bit >> 5] |= c << (bit & 31);
-  if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
 }
 
 __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActArgs a, int nsq) {
@@ -581,31 +581,41 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
   }
   int ea = m > 0.f ? e2m3_block_exp(m) : 0;
   ea = max(-126, min(125, ea));
-  const float sa = pow2f(ea), inva = pow2f(-min(ea, 126));
-  unsigned hi[6] = {0, 0, 0, 0, 0, 0}, lo[6] = {0, 0, 0, 0, 0, 0};
-  float hv[32];
+  const float sa = pow2f(ea);
+  f32x16 ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = xp[2 * i];
+    od[i] = xp[2 * i + 1];
+  }
+  const i32x6 hi = cvt_e2m3x32(ev, od, sa);
+  const f32x32 hv = e2m3x32_values(hi, sa);   // values of the hi term
   float rm = 0.f;
 #pragma unroll
   for (int f = 0; f < 32; ++f) {
-    put6(hi, f, e2m3_round(xp[f] * inva, &hv[f]));
-    hv[f] *= sa;                             // value of the hi term
     xp[f] -= hv[f];                          // remainder
     rm = fmaxf(rm, fabsf(xp[f]));
   }
   int eb = rm > 0.f ? e2m3_block_exp(rm) : ea;
   eb = max(-126, min(125, eb));
-  const float sb = pow2f(eb), invb = pow2f(-min(eb, 126));
+  const float sb = pow2f(eb);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = xp[2 * i];
+    od[i] = xp[2 * i + 1];
+  }
+  const i32x6 lo = cvt_e2m3x32(ev, od, sb);
+  const f32x32 lv = e2m3x32_values(lo, sb);
   float cs = 0.f;                            // sum of this lane's quantized x', in field order
 #pragma unroll
-  for (int f = 0; f < 32; ++f) {
-    float lv;
-    put6(lo, f, e2m3_round(xp[f] * invb, &lv));
-    cs += hv[f] + lv * sb;
-  }
+  for (int f = 0; f < 32; ++f) cs += hv[f] + lv[f];
   unsigned char* q = a.xq[p] + pbase;
-  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 0) * ostep) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 1) * ostep) = u32x4{hi[4], hi[5], lo[0], lo[1]};
-  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 2) * ostep) = u32x4{lo[2], lo[3], lo[4], lo[5]};
+  const u32x4 q0 = {(unsigned)hi[0], (unsigned)hi[1], (unsigned)hi[2], (unsigned)hi[3]};
+  const u32x4 q1 = {(unsigned)hi[4], (unsigned)hi[5], (unsigned)lo[0], (unsigned)lo[1]};
+  const u32x4 q2 = {(unsigned)lo[2], (unsigned)lo[3], (unsigned)lo[4], (unsigned)lo[5]};
+  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 0) * ostep) = q0;
+  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 1) * ostep) = q1;
+  *reinterpret_cast<u32x4*>(q + ((size_t)s * 3 + 2) * ostep) = q2;
   // Block scales with the lane group's operand factor: the sign operand of lane groups 0..2
   // holds the bit b = (s + 1) / 2 as 0.5 * 2^g, so their terms carry 2^(2-g) (the products are
   // 2 b x'); lane group 3 holds s as +-0.5, so its terms carry 2 (the products are s x').
