@@ -24,6 +24,11 @@ namespace bd {
 
 namespace {
 
+// Fixed cost of a piece, in K steps: filling the copy ring and the first activation loads before
+// its first step, and storing its sums after the last.  Measured on the 256-token decode, a
+// 14-step pool piece took as long as about 20 steps of a whole unit.
+constexpr double kPieceCost = 5.0;
+
 bool same_shape(const SplitShape& a, const SplitShape& b) {
   if (a.np != b.np || a.C != b.C || a.Mp != b.Mp || a.nslots != b.nslots ||
       a.slots_avail != b.slots_avail)
@@ -69,7 +74,7 @@ double simulate(const SplitShape& sh, const SplitSched& h, double c_piece, doubl
 SplitSched choose(const SplitShape& sh) {
   // a partial slot (128 rows x Mp tokens of fp32) against the bytes of a step (W_base rows and
   // every variant's sign words)
-  const double c_piece = 1.0;
+  const double c_piece = kPieceCost;
   const double c_part = (double)sh.Mp * kSplitRows * 4 /
                         (double)(kSplitRows * 128 * 2 + sh.nslots * kSplitRows * 16);
   int max_ns = 1;
@@ -129,7 +134,7 @@ SplitSched split_schedule(const SplitShape& sh) {
 double split_schedule_makespan(const SplitShape& sh, const SplitSched& h) {
   const double c_part = (double)sh.Mp * kSplitRows * 4 /
                         (double)(kSplitRows * 128 * 2 + sh.nslots * kSplitRows * 16);
-  return simulate(sh, h, 1.0, c_part);
+  return simulate(sh, h, kPieceCost, c_part);
 }
 
 int split_compute_units() {

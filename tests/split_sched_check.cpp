@@ -90,10 +90,22 @@ int main() {
       const SplitSched h = bd::split_schedule(sh);
       bad += check(sh, h);
       ++cases;
-      // whole units need 260 steps here (the 224-step down blocks and a last round of two
-      // 64-step blocks); the schedule must recover most of it (ideal 204 plus overheads)
+      // whole units leave a tail here (the 224-step down blocks and a last round of 64-step
+      // blocks on few compute units; 204 steps per compute unit on average): the schedule must
+      // end at least 10% sooner than whole units do in the same cost model
+      SplitSched w;
+      memset(&w, 0, sizeof(w));
+      for (int q = 0; q < sh.np; ++q) {
+        w.head[q] = sh.ns[q];
+        w.nheads += (sh.nb[q] + 7) >> 3;
+      }
+      w.sigma = 224;
       const double t = bd::split_schedule_makespan(sh, h);
-      if (t > 225.0) { printf("70B block, Mp %d: makespan %.1f steps\n", mp, t); ++bad; }
+      const double tw = bd::split_schedule_makespan(sh, w);
+      if (t > 0.9 * tw) {
+        printf("70B block, Mp %d: makespan %.1f steps, whole units %.1f\n", mp, t, tw);
+        ++bad;
+      }
     }
   }
   for (int it = 0; it < 400; ++it) {
