@@ -286,7 +286,9 @@ def run_decode(args, torch, bd, config):
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (fp32 accumulate)", "data": "synthetic (seeded; random weights/deltas)",
+        "dtype": {1: "bf16 in, fp32 arithmetic", 2: "bf16 MFMA (fp32 accumulate)",
+                  4: "bf16 MFMA + fp4 x fp6 MFMA (fp32 accumulate)"}.get(path, "bf16"),
+        "data": "synthetic (seeded; random weights/deltas)",
         "config": {"workload": names[config], "config_index": config, "tokens_per_step": m,
                    "segments": [int(v) for v in np.diff(offs)], "active_variants": n_active,
                    "launches_per_step": launches // args.steps,
@@ -347,7 +349,7 @@ def run_prefill(args, torch, bd):
         "metric": "fused BitDelta matmul tokens/s (prefill, bf16 MFMA), 14 variants resident",
         "value": m * 1e3 / ms_step, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp32 accumulate)",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 MFMA (fp32 accumulate)",
         "data": "synthetic (seeded; random weights/deltas)",
         "config": {"workload": "prefill gate+up 28672x8192, 4 requests x 2048 tokens on 4 of 14 variants",
                    "config_index": 4, "tokens_per_step": m, "parallelism": "single GPU"},
