@@ -122,11 +122,17 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+_DTYPES = {}
+
+
 def _dev(t, dtype_name, what):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{what} must be a CUDA/HIP torch tensor")
-    if str(t.dtype) != dtype_name:
+    want = _DTYPES.get(dtype_name)
+    if want is None:
+        want = _DTYPES[dtype_name] = getattr(torch, dtype_name.split(".")[1])
+    if t.dtype is not want:
         raise TypeError(f"{what} must be {dtype_name}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
@@ -244,7 +250,9 @@ def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="a
         parr[i].num_variants = len(variants)
         if x.shape[0] != m or y.shape[0] != m:
             raise ValueError("x and y must have seg_offsets[-1] rows")
-    need = sum(matmul_workspace_bytes(m, int(w.shape[1]), path) for _, w, _, _ in problems)
+    # the library checks the size of a caller's workspace itself; only a missing one is sized here
+    need = 0 if workspace is not None else sum(
+        matmul_workspace_bytes(m, int(w.shape[1]), path) for _, w, _, _ in problems)
     ws_ptr, ws_bytes, ws = _workspace(workspace, need, problems[0][1].device)
     _check(_lib().bitdelta_matmul_grouped(parr, len(problems), m, offs_p, segv_p, segv.size,
                                           _OUT[out_dtype], PATHS[path], ws_ptr, ws_bytes,
@@ -268,7 +276,9 @@ def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf1
     segv, segv_p = _i32(seg_variant)
     varr = _variants_array(variants)
     ws_ptr, ws_bytes, ws = _workspace(
-        workspace, matmul_workspace_bytes(int(x.shape[0]), int(w_base.shape[1])), x.device)
+        workspace,
+        0 if workspace is not None else matmul_workspace_bytes(int(x.shape[0]), int(w_base.shape[1])),
+        x.device)
     _check(_lib().bitdelta_matmul(
         _dev(x, "torch.bfloat16", "x"), _dev(w_base, "torch.bfloat16", "w_base"),
         int(x.shape[0]), int(w_base.shape[0]), int(w_base.shape[1]), varr, len(variants),
