@@ -6,7 +6,8 @@ and the CPU-baseline leg of the benchmark do.  It shares no code with the HIP pa
 What is computed, and where the BitDelta post ("BitDelta: serving 14 Zen models from one GPU
 cluster", hanzo blog, 2026-02-28) defines it:
 
-* compress — "The mathematical foundation": the 1-bit approximation W_ft ~ W_base + alpha*sign(Delta),
+* compress — "The mathematical foundation": the 1-bit approximation W_ft ~ W_base + alpha*sign(Delta)
+  (Delta = W_ft - W_base, also taken from a bf16 weight pair),
   the per-matrix scale alpha = ||Delta||_1 / n (the mean absolute delta over all n elements), and
   one bit per element for the sign.  "Infrastructure details" (delta storage format): sign
   matrices packed eight bits per byte along the input dimension; alpha kept as float32.
@@ -95,6 +96,19 @@ def unpack_signs_ref(words: np.ndarray, d_in: int) -> np.ndarray:
 def compress_ref(delta: np.ndarray):
     """The compression step: (packed sign words, alpha)."""
     return pack_signs_ref(signs_ref(delta)), alpha_ref(delta)
+
+
+def task_vector_ref(w_ft_bits: np.ndarray, w_base_bits: np.ndarray) -> np.ndarray:
+    """Delta = W_ft - W_base for bf16 weights given as uint16 bit patterns ("The mathematical
+    foundation": the fine-tune's delta from the base).  Computed in fp64: exact whenever the two
+    exponents differ by less than 45, otherwise correctly rounded; its sign is always exact and
+    it is zero exactly when the two weights are equal."""
+    return bf16_bits_to_f64(w_ft_bits) - bf16_bits_to_f64(w_base_bits)
+
+
+def compress_from_weights_ref(w_ft_bits: np.ndarray, w_base_bits: np.ndarray):
+    """The compression step applied to the task vector of a (fine-tuned, base) weight pair."""
+    return compress_ref(task_vector_ref(w_ft_bits, w_base_bits))
 
 
 def packed_nbytes_ref(d_out: int, d_in: int) -> int:

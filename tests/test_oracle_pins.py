@@ -226,12 +226,33 @@ def check_batch_invariance(o):
         np.testing.assert_allclose(ys[p], single[0], rtol=1e-13, atol=1e-15)
 
 
+def check_task_vector(o):
+    """Compress from a (fine-tuned, base) bf16 pair: a hand-derived example, equal weights
+    (Delta = 0: every bit +1, alpha 0), and a zero base (the fine-tuned weights themselves)."""
+    g = _load("task_vector.json")
+    k = np.arange(32)
+    w_base = WL.f32_to_bf16_bits(np.stack([np.ones(32), 0.5 + k / 64]).astype(np.float32))
+    w_ft = WL.f32_to_bf16_bits(np.stack([1 + (2 * (k % 4) - 3) / 128, 0.5 + k / 64]).astype(np.float32))
+    words, alpha = o.compress_from_weights_ref(w_ft, w_base)
+    np.testing.assert_array_equal(words, np.asarray(g["words"], dtype=np.uint32))
+    assert float(alpha) == g["alpha"]
+    rng = np.random.default_rng(10)
+    w = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(6, 96)).astype(np.float32))
+    words, alpha = o.compress_from_weights_ref(w, w)
+    assert np.all(words == 0xFFFFFFFF) and float(alpha) == 0.0
+    zero = np.zeros_like(w)
+    words, alpha = o.compress_from_weights_ref(w, zero)
+    ref_words, ref_alpha = o.compress_ref(o.bf16_bits_to_f64(w))
+    np.testing.assert_array_equal(words, ref_words)
+    assert float(alpha) == float(ref_alpha)
+
+
 ALL_CHECKS = [
     check_bit_order_golden, check_tiny_linear_golden, check_storage_arithmetic,
     check_alpha_closed_forms, check_alpha_least_squares, check_laplace_statistics,
     check_signs_and_roundtrip, check_zero_delta_is_plain_product, check_zero_base_isolates_delta,
     check_identity_readback, check_bruteforce_agrees, check_plan_is_stable_sort,
-    check_batch_invariance,
+    check_batch_invariance, check_task_vector,
 ]
 
 
@@ -318,6 +339,10 @@ def _plan_unstable(token_variant, num_variants):  # reverses order inside each g
     return perm, offs, segv
 
 
+def _task_vector_reversed(w_ft_bits, w_base_bits):  # W_base - W_ft
+    return O.bf16_bits_to_f64(w_base_bits) - O.bf16_bits_to_f64(w_ft_bits)
+
+
 _REAL_MATMUL = O.matmul_ref
 _REAL_PLAN = O.plan_segments_ref
 
@@ -333,6 +358,7 @@ MUTANTS = [
     ("reconstruct_ref", _reconstruct_transposed_bits),
     ("matmul_ref", _matmul_wrong_segment),
     ("plan_segments_ref", _plan_unstable),
+    ("task_vector_ref", _task_vector_reversed),
 ]
 
 
