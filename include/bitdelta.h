@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define BITDELTA_ABI_VERSION 3
+#define BITDELTA_ABI_VERSION 4
 #define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
 #define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
 #define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
@@ -136,6 +136,26 @@ size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
 bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
                                   uint32_t* sign_words, uint32_t* sign_words_t128, float* alpha,
                                   void* workspace, size_t workspace_bytes, bitdelta_stream stream);
+
+/*
+ * bitdelta_compress_from_weights — the same compression of the task vector of a bf16 weight pair,
+ * Delta = W_ft - W_base (BitDelta post, "The mathematical foundation": the fine-tune's delta
+ * from the base), without materialising Delta.  The sign of each element is that of the exact
+ * difference (zero, i.e. equal weights, gives +1); alpha sums |Delta| formed in fp64 (exact
+ * unless the two exponents are more than about 45 apart, then rounded once).
+ *
+ *   w_ft, w_base [dev] bf16 [d_out][d_in], 16-byte aligned, finite values.  Read only.
+ *   sign_words, sign_words_t128, alpha, workspace: as for bitdelta_compress (the same workspace
+ *               size; the words are written as whole lines when 16-byte aligned and
+ *               d_in % 128 == 0, else word by word).
+ * Errors: as for bitdelta_compress.  The buffers must not overlap.
+ * ABI 4.
+ */
+bitdelta_status bitdelta_compress_from_weights(const void* w_ft, const void* w_base, int64_t d_out,
+                                               int64_t d_in, uint32_t* sign_words,
+                                               uint32_t* sign_words_t128, float* alpha,
+                                               void* workspace, size_t workspace_bytes,
+                                               bitdelta_stream stream);
 
 /*
  * bitdelta_plan_segments — group a token batch by variant (host only, O(M), no device work).

@@ -77,6 +77,11 @@ def _lib():
         L.bitdelta_compress.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_compress_from_weights.restype = ctypes.c_int
+        L.bitdelta_compress_from_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_size_t, ctypes.c_void_p]
         L.bitdelta_sign_words_t128.restype = ctypes.c_int64
         L.bitdelta_sign_words_t128.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.bitdelta_plan_segments.restype = ctypes.c_int
@@ -170,6 +175,25 @@ def compress(delta, words, alpha, workspace=None, stream=None, tiled=None):
         _dev(delta, "torch.float32", "delta"), d_out, d_in, _dev(words, "torch.int32", "words"),
         tptr, _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)), "bitdelta_compress")
+    return words, alpha
+
+
+def compress_from_weights(w_ft, w_base, words, alpha, workspace=None, stream=None, tiled=None):
+    """compress() of Delta = w_ft - w_base for two bf16 [d_out, d_in] matrices, Delta never
+    formed.  Outputs as for compress()."""
+    import torch
+    d_out, d_in = w_base.shape
+    if tuple(w_ft.shape) != (d_out, d_in):
+        raise ValueError("w_ft and w_base must have the same shape")
+    if workspace is None:
+        workspace = torch.empty(max(compress_workspace_bytes(d_out, d_in), 8) // 8,
+                                dtype=torch.float64, device=w_base.device)
+    tptr = None if tiled is None else _dev(tiled, "torch.int32", "tiled sign words")
+    _check(_lib().bitdelta_compress_from_weights(
+        _dev(w_ft, "torch.bfloat16", "w_ft"), _dev(w_base, "torch.bfloat16", "w_base"), d_out, d_in,
+        _dev(words, "torch.int32", "words"), tptr, _dev(alpha, "torch.float32", "alpha"),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "bitdelta_compress_from_weights")
     return words, alpha
 
 

@@ -576,6 +576,27 @@ bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_i
                                      static_cast<hipStream_t>(stream)));
 }
 
+bitdelta_status bitdelta_compress_from_weights(const void* w_ft, const void* w_base, int64_t d_out,
+                                               int64_t d_in, uint32_t* sign_words,
+                                               uint32_t* sign_words_t128, float* alpha,
+                                               void* workspace, size_t workspace_bytes,
+                                               bitdelta_stream stream) {
+  if (!w_ft || !w_base || !sign_words || !alpha || !workspace) return BITDELTA_ERR_INVALID_ARG;
+  if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim)
+    return BITDELTA_ERR_INVALID_ARG;
+  if (d_in % 32 != 0) return BITDELTA_ERR_SHAPE;
+  if (sign_words_t128 && d_in % 128 != 0) return BITDELTA_ERR_SHAPE;
+  if (!aligned(w_ft, 16) || !aligned(w_base, 16) || !aligned(sign_words, 4) ||
+      !aligned(alpha, 4) || !aligned(workspace, 8) || !aligned(sign_words_t128, 16))
+    return BITDELTA_ERR_ALIGNMENT;
+  if (workspace_bytes < bitdelta_compress_workspace_bytes(d_out, d_in)) return BITDELTA_ERR_WORKSPACE;
+  return map_hip(bd::launch_compress_pair(static_cast<const uint16_t*>(w_ft),
+                                          static_cast<const uint16_t*>(w_base), d_out, d_in,
+                                          sign_words, sign_words_t128, alpha,
+                                          static_cast<double*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 bitdelta_status bitdelta_plan_segments(const int32_t* token_variant, int64_t M,
                                        int32_t num_variants, int32_t* perm,
                                        int32_t* seg_offsets, int32_t* seg_variant,

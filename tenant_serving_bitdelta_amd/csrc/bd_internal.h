@@ -40,6 +40,10 @@ int64_t compress_partials(int64_t d_out, int64_t d_in);
 // none; needs d_in % 128 == 0).
 hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
                            uint32_t* tiled, float* alpha, double* partials, hipStream_t stream);
+// the same outputs for Delta = W_ft - W_base of two bf16 matrices [d_out][d_in]
+hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                                int64_t d_in, uint32_t* words, uint32_t* tiled, float* alpha,
+                                double* partials, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
 // Matmul kernels

@@ -191,6 +191,97 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
   }
 }
 
+// Compression of the task vector of a bf16 weight pair, Delta = W_ft - W_base, in the row-tile
+// form: a workgroup of 8 waves takes 8 rows x 1024 columns, one row per wave; each lane loads 8
+// consecutive weights of both matrices twice (two 1 KiB loads per matrix and wave), so 4 lanes
+// hold the 32 elements of one word, one byte each.  The sign of Delta comes from comparing the
+// two weights through their bit patterns (sign-magnitude order, +0 equal to -0), so it is exact
+// for any pair and any denormal mode; |Delta| is the fp64 difference (exact unless the exponents
+// are more than about 45 apart, then rounded once; never overflows), accumulated in fp64.
+// Words and the tiled copy are gathered in LDS and written as whole lines when the word array is
+// 16-byte aligned and d_in % 128 == 0, else word by word.
+__device__ __forceinline__ int bf16_order(unsigned h) {  // h: 16-bit pattern -> ordered integer
+  return (h & 0x8000u) ? -(int)(h & 0x7FFFu) : (int)(h & 0x7FFFu);
+}
+
+__global__ __launch_bounds__(kTileWaves * 64) void compress_pair_tiles(
+    const uint16_t* __restrict__ w_ft, const uint16_t* __restrict__ w_base, int64_t d_out,
+    int64_t d_in, uint32_t* __restrict__ words, uint32_t* __restrict__ tiled, int vec,
+    double* __restrict__ partials) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t wpr = d_in >> 5;
+  const int64_t ncg = (d_in + kTileCols - 1) / kTileCols;
+  const int64_t ntiles = (d_out + kTileWaves - 1) / kTileWaves * ncg;
+  const unsigned shift = 8u * (unsigned)(lane & 3);
+  __shared__ __align__(16) uint32_t tw[2][kTileWaves][kTileCols / 32];
+  double acc = 0.0;
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x, buf ^= 1) {
+    const int64_t rg = t / ncg, cg = t - rg * ncg;
+    const int64_t r = rg * kTileWaves + wave;
+    u32x4 a[2], b[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t c = cg * kTileCols + u * 512 + lane * 8;
+      const bool ok = r < d_out && c < d_in;
+      a[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_ft + r * d_in + c))
+                : u32x4{0u, 0u, 0u, 0u};
+      b[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_base + r * d_in + c))
+                : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      unsigned byte = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned ha = (a[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const unsigned hb = (b[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        byte |= (unsigned)(bf16_order(ha) >= bf16_order(hb)) << e;
+        acc += fabs((double)__uint_as_float(ha << 16) - (double)__uint_as_float(hb << 16));
+      }
+      unsigned part = byte << shift;
+      part |= __shfl_xor(part, 1);
+      part |= __shfl_xor(part, 2);
+      if ((lane & 3) == 0) tw[buf][wave][u * 16 + (lane >> 2)] = part;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int row = lane >> 3, q = lane & 7;
+      const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
+      if (rr < d_out && wc < wpr) {
+        if (vec) {
+          *reinterpret_cast<u32x4*>(words + rr * wpr + wc) =
+              *reinterpret_cast<const u32x4*>(&tw[buf][row][q * 4]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (wc + e < wpr) words[rr * wpr + wc + e] = tw[buf][row][q * 4 + e];
+        }
+      }
+    } else if (wave == kTileWaves - 1 && tiled) {
+      const int q = lane >> 3, row = lane & 7;
+      const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
+      if (rr < d_out && wc < wpr)
+        *reinterpret_cast<u32x4*>(tiled + ((rr >> 7) * (wpr >> 2) + (wc >> 2)) * 512 +
+                                  (rr & 127) * 4) =
+            *reinterpret_cast<const u32x4*>(&tw[buf][row][q * 4]);
+    }
+  }
+
+  __shared__ double wsum[kTileWaves];
+  acc = wave_sum(acc);
+  if (lane == 0) wsum[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kTileWaves; ++w) sum += wsum[w];
+    partials[blockIdx.x] = sum;
+  }
+}
+
 __global__ __launch_bounds__(kPass2Threads) void compress_pass2(const double* __restrict__ partials,
                                                                int nparts, double n,
                                                                float* __restrict__ alpha) {
@@ -225,9 +316,8 @@ int tile_grid(int64_t d_out, int64_t d_in) {
 }  // namespace
 
 int64_t compress_partials(int64_t d_out, int64_t d_in) {
-  int64_t g = flat_grid(d_out * d_in);
-  if (d_in % 128 == 0) g = std::max<int64_t>(g, tile_grid(d_out, d_in));
-  return g;
+  // the row-tile forms (Delta, or a weight pair with any d_in) and the flat form
+  return std::max<int64_t>(flat_grid(d_out * d_in), tile_grid(d_out, d_in));
 }
 
 hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
@@ -251,6 +341,21 @@ hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compress_pass2, dim3(1), dim3(kPass2Threads), 0, stream, partials, grid,
                      (double)n, alpha);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                                int64_t d_in, uint32_t* words, uint32_t* tiled, float* alpha,
+                                double* partials, hipStream_t stream) {
+  const int grid = tile_grid(d_out, d_in);
+  const int vec = d_in % 128 == 0 && reinterpret_cast<uintptr_t>(words) % 16 == 0;
+  clear_stale_error();
+  hipLaunchKernelGGL(compress_pair_tiles, dim3(grid), dim3(kTileWaves * 64), 0, stream, w_ft,
+                     w_base, d_out, d_in, words, tiled, vec, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compress_pass2, dim3(1), dim3(kPass2Threads), 0, stream, partials, grid,
+                     (double)d_out * (double)d_in, alpha);
   return hipGetLastError();
 }
 

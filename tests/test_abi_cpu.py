@@ -37,7 +37,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.abi_version() == 3
+    assert bd.abi_version() == 4
     for s in range(7):
         assert L.bitdelta_status_string(s)
     assert L.bitdelta_status_string(99) == b"unknown status"
@@ -98,6 +98,27 @@ def test_compress_validation():
     assert _compress(FAKE, 64, 64, FAKE, FAKE, FAKE, ws, tiled=FAKE) == SHAPE
     ws2 = bd.compress_workspace_bytes(64, 128)
     assert _compress(FAKE, 64, 128, FAKE, FAKE, FAKE, ws2, tiled=FAKE + 4) == ALIGN
+
+
+def _compress_pair(ft, base, d_out, d_in, words, alpha, ws, ws_bytes, tiled=None):
+    return L.bitdelta_compress_from_weights(ft, base, d_out, d_in, words, tiled, alpha, ws, ws_bytes,
+                                            None)
+
+
+def test_compress_from_weights_validation():
+    ws = bd.compress_workspace_bytes(64, 96)
+    assert _compress_pair(None, FAKE, 64, 96, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress_pair(FAKE, None, 64, 96, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress_pair(FAKE, FAKE, 64, 96, None, FAKE, FAKE, ws) == INVALID
+    assert _compress_pair(FAKE, FAKE, 0, 96, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress_pair(FAKE, FAKE, 64, 48, FAKE, FAKE, FAKE, ws) == SHAPE
+    assert _compress_pair(FAKE + 8, FAKE, 64, 96, FAKE, FAKE, FAKE, ws) == ALIGN
+    assert _compress_pair(FAKE, FAKE + 8, 64, 96, FAKE, FAKE, FAKE, ws) == ALIGN
+    assert _compress_pair(FAKE, FAKE, 64, 96, FAKE + 2, FAKE, FAKE, ws) == ALIGN
+    assert _compress_pair(FAKE, FAKE, 64, 96, FAKE, FAKE, FAKE, ws - 8) == WORKSPACE
+    assert _compress_pair(FAKE, FAKE, 64, 96, FAKE, FAKE, FAKE, ws, tiled=FAKE) == SHAPE
+    # the row-tile form serves every d_in: its partials fit the compress workspace
+    assert bd.compress_workspace_bytes(64, 96) >= 8 * ((64 + 7) // 8)
 
 
 def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None, ws=FAKE,

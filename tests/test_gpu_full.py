@@ -176,3 +176,26 @@ def test_full_size_prefill_sampled():
         got32 = y32[toks][:, rows].cpu().numpy().astype(np.float64)
         _check_rows(got16, ref, delta_term, 2e-2, 0.75, ("bf16", int(v)))
         _check_rows(got32, ref, delta_term, 5e-3, 0.75, ("f32", int(v)))
+
+
+def test_full_size_compress_from_weights():
+    """Compress from a (fine-tuned, base) bf16 pair at a 70B shape (8192 x 8192, the q / o
+    projection): every sign word and alpha against the oracle's task vector."""
+    d_out, d_in = 8192, 8192
+    base = WL.gpu_normal_bf16(torch, (d_out, d_in), 0.02, WL.substream_seed(6, 0, "q", "w"))
+    delta = WL.gpu_laplace_f32(torch, (d_out, d_in), 3e-4, WL.substream_seed(6, 0, "q", 0, "delta"))
+    ft = (base.float() + delta).to(torch.bfloat16)
+    del delta
+    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+    tiled = torch.empty(bd.sign_words_t128(d_out, d_in), dtype=torch.int32, device="cuda")
+    bd.compress_from_weights(ft, base, words, alpha, tiled=tiled)
+    torch.cuda.synchronize()
+    ft_bits = ft.view(torch.int16).cpu().numpy().view(np.uint16)
+    base_bits = base.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_words, ref_alpha = O.compress_from_weights_ref(ft_bits, base_bits)
+    np.testing.assert_array_equal(words.cpu().numpy().view(np.uint32), ref_words)
+    assert abs(float(alpha.item()) - float(ref_alpha)) <= 1e-6 * float(ref_alpha)
+    got_t = tiled.cpu().numpy().view(np.uint32).reshape(-1, 512)
+    # block (0, 0) of the tiled copy: rows 0..127, words 0..3 of each
+    np.testing.assert_array_equal(got_t[0].reshape(128, 4), ref_words[:128, :4])

@@ -84,6 +84,75 @@ def test_compress_flat_form_unaligned_words():
     np.testing.assert_array_equal(got[real], tile_words_128(ref_words, d_out, d_in)[real])
 
 
+def check_compress_pair(ft_bits, base_bits):
+    """compress_from_weights on the device against the oracle's task-vector compress."""
+    d_out, d_in = ft_bits.shape
+    ft, base = bf16_dev(ft_bits), bf16_dev(base_bits)
+    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+    nt = bd.sign_words_t128(d_out, d_in)
+    tiled = torch.empty(nt, dtype=torch.int32, device="cuda") if nt > 0 else None
+    bd.compress_from_weights(ft, base, words, alpha, tiled=tiled)
+    torch.cuda.synchronize()
+    ref_words, ref_alpha = O.compress_from_weights_ref(ft_bits, base_bits)
+    np.testing.assert_array_equal(words_host(words), ref_words)
+    a = float(alpha.cpu()[0])
+    assert abs(a - float(ref_alpha)) <= 1e-6 * abs(float(ref_alpha)) or a == float(ref_alpha)
+    if tiled is not None:
+        want = tile_words_128(ref_words, d_out, d_in)
+        real = tile_words_128(np.ones_like(ref_words), d_out, d_in) == 1
+        np.testing.assert_array_equal(tiled.cpu().numpy().view(np.uint32)[real], want[real])
+    return words, alpha
+
+
+# d_in % 128 == 0 writes whole lines; other d_in word by word; ragged rows and column groups
+@pytest.mark.parametrize("d_out,d_in,seed", [(1, 32, 31), (3, 64, 32), (17, 96, 33), (64, 1056, 34),
+                                             (255, 512, 35), (130, 3200, 36), (9, 1152, 37),
+                                             (33, 8192, 38)])
+def test_compress_from_weights_shapes(d_out, d_in, seed):
+    rng = np.random.default_rng(seed)
+    base = rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32)
+    ft = base + rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
+    base_bits, ft_bits = WL.f32_to_bf16_bits(base), WL.f32_to_bf16_bits(ft)
+    same = rng.random((d_out, d_in)) < 0.05   # some weights unchanged by the fine-tune
+    ft_bits[same] = base_bits[same]
+    check_compress_pair(ft_bits, base_bits)
+
+
+def test_compress_from_weights_special_values():
+    f = WL.f32_to_bf16_bits
+    base = np.zeros((4, 128), dtype=np.float32)
+    ft = np.zeros((4, 128), dtype=np.float32)
+    # row 0: signed zeros and equal weights (+1), subnormal bf16 differences (exact signs)
+    base[0, :4] = [0.0, -0.0, 1e-39, -1e-39]
+    ft[0, :4] = [-0.0, 0.0, 2e-39, -2e-39]
+    base[0, 4:8] = [1.0, 1.0, -3.0, 2.0 ** -120]
+    ft[0, 4:8] = [1.0, 1.0 + 2 ** -7, -3.0, -(2.0 ** -120)]
+    # row 1: exponents far apart (the fp32 difference rounds; the sign stays exact)
+    base[1, :4] = [2.0 ** 60, -(2.0 ** 60), 1.0, -1.0]
+    ft[1, :4] = [2.0 ** 60 + 2.0 ** 53, -(2.0 ** 60), 1.0 + 2.0 ** -7, -1.0 - 2.0 ** -7]
+    ft[1, 4:8] = [2.0 ** -100, -(2.0 ** -100), 3e38, -3e38]
+    # rows 2, 3: every weight changed upward / downward
+    base[2] = np.linspace(-1, 1, 128)
+    ft[2] = base[2] + 0.25
+    base[3] = np.linspace(-1, 1, 128)
+    ft[3] = base[3] - 0.25
+    words, alpha = check_compress_pair(f(ft), f(base))
+    w = words_host(words)
+    assert np.all(w[2] == 0xFFFFFFFF) and np.all(w[3] == 0)
+
+
+def test_compress_from_weights_equal_and_repeatable():
+    rng = np.random.default_rng(39)
+    base_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(40, 1024)).astype(np.float32))
+    words, alpha = check_compress_pair(base_bits, base_bits)
+    assert float(alpha.cpu()[0]) == 0.0 and np.all(words_host(words) == 0xFFFFFFFF)
+    ft_bits = WL.f32_to_bf16_bits((rng.normal(0, 0.02, size=(40, 1024))).astype(np.float32))
+    w1, a1 = check_compress_pair(ft_bits, base_bits)
+    w2, a2 = check_compress_pair(ft_bits, base_bits)
+    assert torch.equal(w1, w2) and torch.equal(a1, a2)
+
+
 def test_compress_special_values():
     d = np.zeros((4, 64), dtype=np.float32)
     d[0, :8] = [-0.0, 0.0, -1e-45, 1e-45, -1e-40, 1e-40, -1.17e-38, 3.0]
