@@ -141,8 +141,9 @@ bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_i
  * bitdelta_compress_from_weights — the same compression of the task vector of a bf16 weight pair,
  * Delta = W_ft - W_base (BitDelta post, "The mathematical foundation": the fine-tune's delta
  * from the base), without materialising Delta.  The sign of each element is that of the exact
- * difference (zero, i.e. equal weights, gives +1); alpha sums |Delta| formed in fp64 (exact
- * unless the two exponents are more than about 45 apart, then rounded once).
+ * difference (zero, i.e. equal weights, gives +1); alpha sums |Delta| formed in fp32 (exact
+ * unless the two exponents are more than 16 apart, then rounded once), 4 consecutive elements
+ * in fp32 and those sums in fp64 (weights below 4e37 in magnitude keep every sum finite).
  *
  *   w_ft, w_base [dev] bf16 [d_out][d_in], 16-byte aligned, finite values.  Read only.
  *   sign_words, sign_words_t128, alpha, workspace: as for bitdelta_compress (the same workspace

@@ -194,16 +194,13 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
 // Compression of the task vector of a bf16 weight pair, Delta = W_ft - W_base, in the row-tile
 // form: a workgroup of 8 waves takes 8 rows x 1024 columns, one row per wave; each lane loads 8
 // consecutive weights of both matrices twice (two 1 KiB loads per matrix and wave), so 4 lanes
-// hold the 32 elements of one word, one byte each.  The sign of Delta comes from comparing the
-// two weights through their bit patterns (sign-magnitude order, +0 equal to -0), so it is exact
-// for any pair and any denormal mode; |Delta| is the fp64 difference (exact unless the exponents
-// are more than about 45 apart, then rounded once; never overflows), accumulated in fp64.
+// hold the 32 elements of one word, one byte each.  Delta is the fp32 difference of the two
+// weights (bf16 values widen exactly; the difference is exact unless their exponents are more
+// than 16 apart, then rounded once, and it keeps the sign of the exact difference: zero only for
+// equal weights, subnormals kept since fp32 denormals are not flushed); 4 consecutive |Delta| are
+// added in fp32 and accumulated in fp64, as in the kernels above.
 // Words and the tiled copy are gathered in LDS and written as whole lines when the word array is
 // 16-byte aligned and d_in % 128 == 0, else word by word.
-__device__ __forceinline__ int bf16_order(unsigned h) {  // h: 16-bit pattern -> ordered integer
-  return (h & 0x8000u) ? -(int)(h & 0x7FFFu) : (int)(h & 0x7FFFu);
-}
-
 __global__ __launch_bounds__(kTileWaves * 64) void compress_pair_tiles(
     const uint16_t* __restrict__ w_ft, const uint16_t* __restrict__ w_base, int64_t d_out,
     int64_t d_in, uint32_t* __restrict__ words, uint32_t* __restrict__ tiled, int vec,
@@ -234,13 +231,18 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_pair_tiles(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       unsigned byte = 0u;
+      float grp[2] = {0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const unsigned ha = (a[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const unsigned hb = (b[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        byte |= (unsigned)(bf16_order(ha) >= bf16_order(hb)) << e;
-        acc += fabs((double)__uint_as_float(ha << 16) - (double)__uint_as_float(hb << 16));
+        const unsigned wa = a[u][e >> 1], wb = b[u][e >> 1];
+        const float fa = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+        const float fb = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+        const float d = fa - fb;
+        byte |= (is_negative(d) ^ 1u) << e;
+        grp[e >> 2] += fabsf(d);
       }
+      acc += (double)grp[0];
+      acc += (double)grp[1];
       unsigned part = byte << shift;
       part |= __shfl_xor(part, 1);
       part |= __shfl_xor(part, 2);

@@ -131,7 +131,9 @@ def test_compress_from_weights_special_values():
     # row 1: exponents far apart (the fp32 difference rounds; the sign stays exact)
     base[1, :4] = [2.0 ** 60, -(2.0 ** 60), 1.0, -1.0]
     ft[1, :4] = [2.0 ** 60 + 2.0 ** 53, -(2.0 ** 60), 1.0 + 2.0 ** -7, -1.0 - 2.0 ** -7]
-    ft[1, 4:8] = [2.0 ** -100, -(2.0 ** -100), 3e38, -3e38]
+    ft[1, 4:8] = [2.0 ** -100, -(2.0 ** -100), 5e37, -5e37]
+    base[1, 8:10] = [1.0, -1.0]
+    ft[1, 8:10] = [2.0 ** -30, -(2.0 ** -30)]
     # rows 2, 3: every weight changed upward / downward
     base[2] = np.linspace(-1, 1, 128)
     ft[2] = base[2] + 0.25
