@@ -18,7 +18,8 @@ cluster", hanzo blog, 2026-02-28) defines it:
 
 Readings taken where the post is silent (each is listed in the design notes):
 
-* alpha is one scalar per matrix (the formula averages over all n elements).
+* alpha is one scalar per matrix (the formula averages over all n elements); the per-row form
+  (``alpha_rows_ref``: the same mean taken over each output row) is offered beside it.
 * alpha = float32 round-to-nearest-even of (exact sum of |Delta|) / n.  The sum is exact
   (``math.fsum``) up to ``FSUM_MAX`` elements and numpy's pairwise fp64 sum above that.
 * sign(0) = +1, including -0.0; negative subnormals are negative.
@@ -63,6 +64,18 @@ def alpha_ref(delta: np.ndarray) -> np.float32:
     return np.float32(total / n)
 
 
+def alpha_rows_ref(delta: np.ndarray) -> np.ndarray:
+    """Per-output-row scales, the other granularity the post allows (its conceptual fused kernel
+    in "Serving architecture" takes alpha of shape [d_out] or a scalar; "Infrastructure details"
+    stores one float32 per output dimension): alpha_r = mean over the d_in elements of row r of
+    |Delta_rc|, the exact row sum divided by d_in and rounded once to float32."""
+    a = np.abs(np.asarray(delta, dtype=np.float64))
+    if a.ndim != 2 or a.shape[1] == 0:
+        raise ValueError("alpha rows need a [d_out, d_in] matrix with d_in > 0")
+    d_in = a.shape[1]
+    return np.array([np.float32(math.fsum(row.tolist()) / d_in) for row in a], dtype=np.float32)
+
+
 def signs_ref(delta: np.ndarray) -> np.ndarray:
     """sign(Delta) as int8 in {-1,+1}.  The post reduces each delta to "positive or negative";
     zero (either sign of zero) maps to +1 by convention; a value is negative only if it is
@@ -98,6 +111,11 @@ def compress_ref(delta: np.ndarray):
     return pack_signs_ref(signs_ref(delta)), alpha_ref(delta)
 
 
+def compress_rows_ref(delta: np.ndarray):
+    """The compression step with per-output-row scales: (packed sign words, alpha [d_out])."""
+    return pack_signs_ref(signs_ref(delta)), alpha_rows_ref(delta)
+
+
 def task_vector_ref(w_ft_bits: np.ndarray, w_base_bits: np.ndarray) -> np.ndarray:
     """Delta = W_ft - W_base for bf16 weights given as uint16 bit patterns ("The mathematical
     foundation": the fine-tune's delta from the base).  Computed in fp64: exact whenever the two
@@ -121,11 +139,19 @@ def packed_nbytes_ref(d_out: int, d_in: int) -> int:
 # ----------------------------------------------------------------------------------------------
 
 def reconstruct_ref(w_base: np.ndarray, words: np.ndarray, alpha) -> np.ndarray:
-    """W_eff = W_base + alpha * sign(Delta) in fp64, with alpha the stored float32 value and the
+    """W_eff = W_base + alpha * sign(Delta) in fp64, with alpha the stored float32 value (one
+    scalar, or one per output row: W_eff[r] = W_base[r] + alpha[r] * sign(Delta[r])) and the
     signs unpacked from the stored bits."""
     wb = np.asarray(w_base, dtype=np.float64)
     s = unpack_signs_ref(words, wb.shape[1]).astype(np.float64)
-    return wb + np.float64(np.float32(alpha)) * s
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64)
+    if a.ndim == 1:
+        if a.shape[0] != wb.shape[0]:
+            raise ValueError("alpha rows must have one entry per output row")
+        a = a[:, None]
+    elif a.ndim != 0:
+        raise ValueError("alpha is a scalar or a [d_out] vector")
+    return wb + a * s
 
 
 def fused_linear_ref(x: np.ndarray, w_base: np.ndarray, words: np.ndarray, alpha) -> np.ndarray:
@@ -188,7 +214,9 @@ def matmul_bruteforce(x, w_base, variants, token_variant):
                 if v >= 0:
                     words, alpha = variants[v]
                     bit = (int(words[r][k // 32]) >> (k % 32)) & 1
-                    weff += float(np.float32(alpha)) * (1.0 if bit else -1.0)
+                    a = np.asarray(alpha, dtype=np.float32)
+                    scale = float(a) if a.ndim == 0 else float(a[r])
+                    weff += scale * (1.0 if bit else -1.0)
                 acc += xt[k] * weff
             row_out.append(acc)
         y.append(row_out)

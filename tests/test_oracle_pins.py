@@ -247,12 +247,72 @@ def check_task_vector(o):
     assert float(alpha) == float(ref_alpha)
 
 
+def check_alpha_rows(o):
+    """Per-output-row scales: hand-derived closed forms, one row equals the per-matrix scale,
+    each alpha_r is the least-squares scale of its row for the row's signs (numpy's lstsq on the
+    one-column system), the mean of equal-length rows' scales is the matrix scale, and the signs
+    do not depend on the granularity."""
+    k = np.arange(32)
+    d = np.zeros((3, 32), dtype=np.float32)
+    d[0] = np.where(k % 3 == 0, -0.5, 0.5)        # constant magnitude: 0.5
+    d[1] = np.where(k % 2 == 0, 1, -1) * k / 32   # |d| = k/32: sum 496/32 over 32 -> 0.484375
+    d[2, 9] = -3.0                                # one element: 3/32
+    a = o.alpha_rows_ref(d)
+    assert a.shape == (3,) and a.dtype == np.float32
+    assert [float(v) for v in a] == [0.5, 0.484375, 0.09375]
+    rng = np.random.default_rng(21)
+    one = rng.laplace(0, 1e-3, size=(1, 160)).astype(np.float32)
+    assert float(o.alpha_rows_ref(one)[0]) == float(o.alpha_ref(one))
+    d = rng.laplace(0, 3e-4, size=(12, 96)).astype(np.float32)
+    d[3] *= 40.0                                  # rows of very different scale
+    words, a = o.compress_rows_ref(d)
+    s = o.unpack_signs_ref(words, d.shape[1]).astype(np.float64)
+    for r in range(d.shape[0]):
+        best = np.linalg.lstsq(s[r][:, None], d[r].astype(np.float64), rcond=None)[0][0]
+        assert abs(float(a[r]) - best) <= 1e-6 * abs(best)
+    assert abs(float(np.mean(a.astype(np.float64))) - float(o.alpha_ref(d))) <= 1e-6 * float(o.alpha_ref(d))
+    np.testing.assert_array_equal(words, o.compress_ref(d)[0])
+
+
+def check_alpha_rows_linear(o):
+    """The fused linear with per-row scales: with W_base = 0 and x = the unit vector e_j,
+    y[r] = alpha_r * sign(Delta[r][j]) (hand-checkable); equal row scales reduce to the scalar
+    form; the pure-loop brute force agrees on a mixed batch of per-row and per-matrix variants."""
+    d = np.array([[0.5] * 32, [-1.0] * 32, [0.25 if c % 2 else -0.25 for c in range(32)]],
+                 dtype=np.float32)
+    words, a = o.compress_rows_ref(d)
+    w0 = np.zeros((3, 32))
+    for j in (0, 1):
+        x = np.zeros((1, 32))
+        x[0, j] = 1.0
+        y = o.fused_linear_ref(x, w0, words, a)
+        want = [0.5, -1.0, 0.25 if j % 2 else -0.25]
+        assert [float(v) for v in y[0]] == want
+    rng = np.random.default_rng(22)
+    w = rng.normal(0, 0.02, size=(5, 64))
+    dd = rng.laplace(0, 1e-3, size=(5, 64)).astype(np.float32)
+    words, _ = o.compress_ref(dd)
+    x = rng.normal(size=(4, 64))
+    same = np.full(5, np.float32(7e-4), dtype=np.float32)
+    np.testing.assert_allclose(o.fused_linear_ref(x, w, words, same),
+                               o.fused_linear_ref(x, w, words, np.float32(7e-4)), rtol=0, atol=1e-15)
+    variants = [o.compress_rows_ref(rng.laplace(0, 1e-3, size=(5, 64)).astype(np.float32)),
+                o.compress_ref(rng.laplace(0, 1e-3, size=(5, 64)).astype(np.float32))]
+    x = rng.normal(size=(7, 64))
+    ids = np.array([1, 0, -1, 0, 1, 0, 0])
+    perm, offs, segv = o.plan_segments_ref(ids, 2)
+    ys = o.matmul_ref(x[perm], w, variants, offs, segv)
+    y = np.empty_like(ys)
+    y[perm] = ys
+    np.testing.assert_allclose(y, o.matmul_bruteforce(x, w, variants, ids), rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_bit_order_golden, check_tiny_linear_golden, check_storage_arithmetic,
     check_alpha_closed_forms, check_alpha_least_squares, check_laplace_statistics,
     check_signs_and_roundtrip, check_zero_delta_is_plain_product, check_zero_base_isolates_delta,
     check_identity_readback, check_bruteforce_agrees, check_plan_is_stable_sort,
-    check_batch_invariance, check_task_vector,
+    check_batch_invariance, check_task_vector, check_alpha_rows, check_alpha_rows_linear,
 ]
 
 
@@ -343,6 +403,21 @@ def _task_vector_reversed(w_ft_bits, w_base_bits):  # W_base - W_ft
     return O.bf16_bits_to_f64(w_base_bits) - O.bf16_bits_to_f64(w_ft_bits)
 
 
+def _alpha_rows_of_columns(delta):  # means over columns instead of rows
+    return np.abs(np.asarray(delta, dtype=np.float64)).mean(axis=0).astype(np.float32)
+
+
+def _alpha_rows_divide_by_n(delta):  # row sums divided by the matrix size
+    a = np.abs(np.asarray(delta, dtype=np.float64))
+    return (a.sum(axis=1) / a.size).astype(np.float32)
+
+
+def _reconstruct_first_row_alpha(w_base, words, alpha):  # alpha[0] used for every row
+    a = np.asarray(alpha, dtype=np.float32)
+    return _REAL_RECONSTRUCT(w_base, words, a if a.ndim == 0 else a[0])
+
+
+_REAL_RECONSTRUCT = O.reconstruct_ref
 _REAL_MATMUL = O.matmul_ref
 _REAL_PLAN = O.plan_segments_ref
 
@@ -359,6 +434,9 @@ MUTANTS = [
     ("matmul_ref", _matmul_wrong_segment),
     ("plan_segments_ref", _plan_unstable),
     ("task_vector_ref", _task_vector_reversed),
+    ("alpha_rows_ref", _alpha_rows_of_columns),
+    ("alpha_rows_ref", _alpha_rows_divide_by_n),
+    ("reconstruct_ref", _reconstruct_first_row_alpha),
 ]
 
 
