@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define BITDELTA_ABI_VERSION 4
+#define BITDELTA_ABI_VERSION 5
 #define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
 #define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
 #define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
@@ -68,14 +68,18 @@ typedef enum {
   BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
   BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp6 MFMA on a
                               * two-term fp6 split of alpha * x (per-32-column power-of-two
-                              * scales); needs workspace and tiled sign words                 */
+                              * scales); needs workspace and tiled sign words, and per-matrix
+                              * alpha (AUTO runs a batch with a per-row variant on STREAM)    */
 } bitdelta_path;
 
 /* One compressed variant of one weight matrix: the output of bitdelta_compress. */
 typedef struct {
   const uint32_t* sign_words;      /* [dev] d_out * d_in / 32 words, row-major, 4-byte aligned */
   const uint32_t* sign_words_t128; /* [dev] tiled copy (layout above), 16-byte aligned, or NULL */
-  const float* alpha;              /* [dev] one float32: the per-matrix scale                  */
+  const float* alpha;              /* [dev] the scale: one float32, or d_out (alpha_per_row)   */
+  int32_t alpha_per_row;           /* 0: one scale per matrix (bitdelta_compress); 1: one per
+                                    * output row, alpha[r] for row r (bitdelta_compress_rows);
+                                    * other values: INVALID_ARG.  ABI 5.                      */
 } bitdelta_variant;
 
 /* One linear layer of a grouped matmul: every problem of a call sees the same token batch
@@ -157,6 +161,32 @@ bitdelta_status bitdelta_compress_from_weights(const void* w_ft, const void* w_b
                                                uint32_t* sign_words_t128, float* alpha,
                                                void* workspace, size_t workspace_bytes,
                                                bitdelta_stream stream);
+
+/* Device workspace bytes bitdelta_compress_rows needs for this shape (one fp64 partial sum per
+ * row and 1024-column group), 0 for an invalid shape. */
+size_t bitdelta_compress_rows_workspace_bytes(int64_t d_out, int64_t d_in);
+
+/*
+ * bitdelta_compress_rows — compression with one scale per output row, the other granularity the
+ * post allows (BitDelta post, "Serving architecture": the conceptual fused kernel takes alpha of
+ * shape [d_out] or a scalar; "Infrastructure details": alpha kept as float32, one per output
+ * dimension): alpha[r] = the mean of |Delta| over the d_in elements of row r.  The sign bits are
+ * those of bitdelta_compress.  Use the result with alpha_per_row = 1 in bitdelta_variant.
+ *
+ *   delta, sign_words, sign_words_t128: as for bitdelta_compress (any 4-byte-aligned word array;
+ *               whole lines when 16-byte aligned and d_in % 128 == 0, else word by word).
+ *   alpha       [dev] out: float32 [d_out], 4-byte aligned: row r's sum of |Delta| (4
+ *               consecutive elements added in fp32, those sums in fp64, the row's 1024-column
+ *               groups in column order, so repeated calls are bit-identical) divided by d_in and
+ *               rounded once to float32.
+ *   workspace   [dev] at least bitdelta_compress_rows_workspace_bytes(d_out, d_in) bytes,
+ *               8-byte aligned; scratch only.
+ * Errors: as for bitdelta_compress.  The buffers must not overlap.  ABI 5.
+ */
+bitdelta_status bitdelta_compress_rows(const float* delta, int64_t d_out, int64_t d_in,
+                                       uint32_t* sign_words, uint32_t* sign_words_t128,
+                                       float* alpha, void* workspace, size_t workspace_bytes,
+                                       bitdelta_stream stream);
 
 /*
  * bitdelta_plan_segments — group a token batch by variant (host only, O(M), no device work).

@@ -14,6 +14,7 @@ import numpy as np
 
 __all__ = [
     "BitDeltaError", "lib", "abi_version", "sign_words", "compress_workspace_bytes",
+    "compress_rows", "compress_rows_workspace_bytes",
     "compress", "plan_segments", "matmul", "matmul_grouped", "auto_path", "PATHS",
     "matmul_workspace_bytes", "sign_words_t128",
 ]
@@ -38,7 +39,7 @@ class BitDeltaError(RuntimeError):
 
 class _Variant(ctypes.Structure):
     _fields_ = [("sign_words", ctypes.c_void_p), ("sign_words_t128", ctypes.c_void_p),
-                ("alpha", ctypes.c_void_p)]
+                ("alpha", ctypes.c_void_p), ("alpha_per_row", ctypes.c_int32)]
 
 
 class _Problem(ctypes.Structure):
@@ -82,6 +83,12 @@ def _lib():
                                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                      ctypes.c_void_p, ctypes.c_void_p,
                                                      ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_compress_rows.restype = ctypes.c_int
+        L.bitdelta_compress_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_compress_rows_workspace_bytes.restype = ctypes.c_size_t
+        L.bitdelta_compress_rows_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.bitdelta_sign_words_t128.restype = ctypes.c_int64
         L.bitdelta_sign_words_t128.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.bitdelta_plan_segments.restype = ctypes.c_int
@@ -197,6 +204,28 @@ def compress_from_weights(w_ft, w_base, words, alpha, workspace=None, stream=Non
     return words, alpha
 
 
+def compress_rows_workspace_bytes(d_out: int, d_in: int) -> int:
+    return int(_lib().bitdelta_compress_rows_workspace_bytes(d_out, d_in))
+
+
+def compress_rows(delta, words, alpha, workspace=None, stream=None, tiled=None):
+    """compress() with one scale per output row: ``alpha`` is float32 [d_out]; pass the result to
+    matmul as (words, alpha[, tiled]) and it is applied row by row."""
+    import torch
+    d_out, d_in = delta.shape
+    if alpha.numel() != d_out:
+        raise ValueError("alpha must hold one float32 per output row")
+    if workspace is None:
+        workspace = torch.empty(max(compress_rows_workspace_bytes(d_out, d_in), 8) // 8,
+                                dtype=torch.float64, device=delta.device)
+    tptr = None if tiled is None else _dev(tiled, "torch.int32", "tiled sign words")
+    _check(_lib().bitdelta_compress_rows(
+        _dev(delta, "torch.float32", "delta"), d_out, d_in, _dev(words, "torch.int32", "words"),
+        tptr, _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "bitdelta_compress_rows")
+    return words, alpha
+
+
 def plan_segments(token_variant, num_variants: int):
     """Stable grouping of tokens by variant (base -1 first).  Returns numpy int32
     (perm, seg_offsets, seg_variant)."""
@@ -236,8 +265,9 @@ def auto_path(m: int, seg_offsets, seg_variant) -> int:
     return int(_lib().bitdelta_auto_path(m, op, vp, v.size))
 
 
-def _variants_array(variants):
-    """variants: list of (words, alpha) or (words, alpha, tiled_words) (or None for unused)."""
+def _variants_array(variants, d_out):
+    """variants: list of (words, alpha) or (words, alpha, tiled_words) (or None for unused);
+    alpha holds one float32 (per matrix) or d_out of them (per output row)."""
     arr = (_Variant * max(len(variants), 1))()
     for i, item in enumerate(variants):
         if item is None:
@@ -245,6 +275,10 @@ def _variants_array(variants):
         words, alpha = item[0], item[1]
         arr[i].sign_words = _dev(words, "torch.int32", "sign words")
         arr[i].alpha = _dev(alpha, "torch.float32", "alpha")
+        n = alpha.numel()
+        if n != 1 and n != d_out:
+            raise ValueError(f"variant {i}: alpha must hold 1 or d_out = {d_out} values, not {n}")
+        arr[i].alpha_per_row = 1 if n > 1 else 0
         if len(item) > 2 and item[2] is not None:
             arr[i].sign_words_t128 = _dev(item[2], "torch.int32", "tiled sign words")
     return arr
@@ -264,7 +298,7 @@ def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="a
     parr = (_Problem * len(problems))()
     keep = []
     for i, (x, w, y, variants) in enumerate(problems):
-        varr = _variants_array(variants)
+        varr = _variants_array(variants, w.shape[0])
         keep.append(varr)
         parr[i].x = _dev(x, "torch.bfloat16", "x")
         parr[i].w_base = _dev(w, "torch.bfloat16", "w_base")
@@ -298,7 +332,7 @@ def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf1
         return y
     offs, offs_p = _i32(seg_offsets)
     segv, segv_p = _i32(seg_variant)
-    varr = _variants_array(variants)
+    varr = _variants_array(variants, w_base.shape[0])
     ws_ptr, ws_bytes, ws = _workspace(
         workspace,
         0 if workspace is not None else matmul_workspace_bytes(int(x.shape[0]), int(w_base.shape[1])),

@@ -62,6 +62,7 @@ bitdelta_status check_problem(const bitdelta_problem& p, int64_t M,
     if (s.variant >= 0) {
       const bitdelta_variant& v = p.variants[s.variant];
       if (!v.sign_words || !v.alpha) return BITDELTA_ERR_INVALID_ARG;
+      if (v.alpha_per_row != 0 && v.alpha_per_row != 1) return BITDELTA_ERR_INVALID_ARG;
       if (!aligned(v.sign_words, 4) || !aligned(v.alpha, 4)) return BITDELTA_ERR_ALIGNMENT;
     }
   }
@@ -103,6 +104,7 @@ bool split_eligible(const bitdelta_problem* probs, int np, int64_t M,
       if (s.variant < 0) continue;
       const uint32_t* t = P.variants[s.variant].sign_words_t128;
       if (!t || !aligned(t, 16)) return false;
+      if (P.variants[s.variant].alpha_per_row) return false;  // alpha is folded into x
     }
   }
   return true;
@@ -129,6 +131,7 @@ bitdelta_status run_gemv(const bitdelta_problem* probs, int np, int64_t M,
         if (s.variant != last) {
           a.words[nslot] = P.variants[s.variant].sign_words;
           a.alpha[nslot] = P.variants[s.variant].alpha;
+          if (P.variants[s.variant].alpha_per_row) a.alpha_rows |= 1u << nslot;
           ++nslot;
         }
         slot = nslot - 1;
@@ -200,9 +203,11 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
         S.d_out = (int)P.d_out;
         S.d_in = (int)P.d_in;
         S.block_begin = blocks;
+        S.alpha_rows = 0;
         for (int s = 0; s < (int)slot_var.size(); ++s) {
           S.words[s] = P.variants[slot_var[s]].sign_words;
           S.alpha[s] = P.variants[slot_var[s]].alpha;
+          if (P.variants[slot_var[s]].alpha_per_row) S.alpha_rows |= 1u << s;
         }
         if (slot_var.empty()) {
           // W_base is at least 16x larger than a sign-word matrix of the same shape
@@ -508,9 +513,11 @@ bitdelta_status run_prefill(const bitdelta_problem* probs, int np,
       a.n_mtiles = (int)(m1 - m0);
       a.n_ntiles = (int)((P.d_out + bd::kPrefillBN - 1) / bd::kPrefillBN);
       a.vec_signs = P.d_in % 128 == 0;
+      a.alpha_rows = 0;
       for (int s = 0; s < (int)slot_var.size(); ++s) {
         a.words[s] = P.variants[slot_var[s]].sign_words;
         a.alpha[s] = P.variants[slot_var[s]].alpha;
+        if (P.variants[slot_var[s]].alpha_per_row) a.alpha_rows |= 1u << s;
         if (!aligned(a.words[s], 16)) a.vec_signs = 0;
       }
       bitdelta_status r = map_hip(bd::launch_prefill(a, st));
@@ -593,6 +600,29 @@ bitdelta_status bitdelta_compress_from_weights(const void* w_ft, const void* w_b
   return map_hip(bd::launch_compress_pair(static_cast<const uint16_t*>(w_ft),
                                           static_cast<const uint16_t*>(w_base), d_out, d_in,
                                           sign_words, sign_words_t128, alpha,
+                                          static_cast<double*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t bitdelta_compress_rows_workspace_bytes(int64_t d_out, int64_t d_in) {
+  if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim || d_in % 32 != 0) return 0;
+  return (size_t)bd::compress_rows_partials(d_out, d_in) * sizeof(double);
+}
+
+bitdelta_status bitdelta_compress_rows(const float* delta, int64_t d_out, int64_t d_in,
+                                       uint32_t* sign_words, uint32_t* sign_words_t128,
+                                       float* alpha, void* workspace, size_t workspace_bytes,
+                                       bitdelta_stream stream) {
+  if (!delta || !sign_words || !alpha || !workspace) return BITDELTA_ERR_INVALID_ARG;
+  if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim) return BITDELTA_ERR_INVALID_ARG;
+  if (d_in % 32 != 0) return BITDELTA_ERR_SHAPE;
+  if (sign_words_t128 && d_in % 128 != 0) return BITDELTA_ERR_SHAPE;
+  if (!aligned(delta, 16) || !aligned(sign_words, 4) || !aligned(alpha, 4) ||
+      !aligned(workspace, 8) || !aligned(sign_words_t128, 16))
+    return BITDELTA_ERR_ALIGNMENT;
+  if (workspace_bytes < bitdelta_compress_rows_workspace_bytes(d_out, d_in))
+    return BITDELTA_ERR_WORKSPACE;
+  return map_hip(bd::launch_compress_rows(delta, d_out, d_in, sign_words, sign_words_t128, alpha,
                                           static_cast<double*>(workspace),
                                           static_cast<hipStream_t>(stream)));
 }

@@ -36,6 +36,10 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
 // fp64 partials (workspace doubles) pass 1 may write for a d_out x d_in matrix, whichever of
 // its two forms runs
 int64_t compress_partials(int64_t d_out, int64_t d_in);
+int64_t compress_rows_partials(int64_t d_out, int64_t d_in);
+hipError_t launch_compress_rows(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
+                                uint32_t* tiled, float* alpha, double* partials,
+                                hipStream_t stream);
 // words: row-major [d_out][d_in/32]; tiled: optional copy in the 128-row tiled layout (NULL for
 // none; needs d_in % 128 == 0).
 hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
@@ -61,6 +65,7 @@ struct GemvArgs {
   int tok_slot[4];
   const uint32_t* words[4];
   const float* alpha[4];
+  unsigned alpha_rows;  // bit s set: slot s has one alpha per output row
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
@@ -76,7 +81,7 @@ struct StreamProblem {
   void* y;
   int d_out, d_in;
   int block_begin;
-  int pad_;
+  unsigned alpha_rows;  // bit s set: slot s has one alpha per output row
   const uint32_t* words[kMaxSlots];
   const float* alpha[kMaxSlots];
 };
@@ -102,6 +107,7 @@ struct PrefillArgs {
   void* y;
   int d_out, d_in, y_f32, n_mtiles, n_ntiles;
   int vec_signs;                       // every words[] 16-byte aligned and d_in % 128 == 0
+  unsigned alpha_rows;                 // bit s set: slot s has one alpha per output row
   const uint32_t* words[kMaxSlots];
   const float* alpha[kMaxSlots];
   // per M-tile: first x row, rows in the tile (1..256), variant slot (-1 = base)

@@ -124,11 +124,15 @@ __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restri
 }
 
 // Row-tile form.  Tile t covers rows 8 (t / ncg) .. +7 and columns 1024 (t % ncg) .. +1023
-// (ncg = ceil(d_in / 1024)); rows past d_out and columns past d_in are skipped.  wpr = d_in / 32
-// is a multiple of 4, so a 4-word group is wholly inside or outside the row.
+// (ncg = ceil(d_in / 1024)); rows past d_out and columns past d_in are skipped.  Per-matrix
+// scale (kRows = false): d_in % 128 == 0 and 16-byte aligned words, so a 4-word group is wholly
+// inside or outside the row; one fp64 partial per workgroup.  Per-row scales (kRows = true): any
+// d_in % 32 == 0 (words stored one by one unless vec), one fp64 partial per row and column
+// group, partials[r * ncg + cg].
+template <bool kRows>
 __global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
     const float* __restrict__ delta, int64_t d_out, int64_t d_in, uint32_t* __restrict__ words,
-    uint32_t* __restrict__ tiled, double* __restrict__ partials) {
+    uint32_t* __restrict__ tiled, int vec_words, double* __restrict__ partials) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -151,23 +155,40 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
                  ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(delta + r * d_in + c))
                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    double tacc = 0.0;
 #pragma unroll
     for (int u = 0; u < kTileCols / 256; ++u) {
-      acc += (double)((fabsf(v[u][0]) + fabsf(v[u][1])) + (fabsf(v[u][2]) + fabsf(v[u][3])));
+      const double grp =
+          (double)((fabsf(v[u][0]) + fabsf(v[u][1])) + (fabsf(v[u][2]) + fabsf(v[u][3])));
+      if (kRows)
+        tacc += grp;
+      else
+        acc += grp;
       unsigned part = nonneg_nibble(v[u]) << shift;
       part |= __shfl_xor(part, 1);
       part |= __shfl_xor(part, 2);
       part |= __shfl_xor(part, 4);
       if ((lane & 7) == 0) tw[buf][wave][u * 8 + (lane >> 3)] = part;
     }
+    if (kRows) {
+      tacc = wave_sum(tacc);
+      if (lane == 0 && r < d_out) partials[r * ncg + cg] = tacc;
+    }
     __syncthreads();
     if (wave == 0) {
       // plain words: lane = (row, 4-word group); the 8 lanes of a row fill its 128-byte line
       const int row = lane >> 3, q = lane & 7;
       const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
-      if (rr < d_out && wc < wpr)
-        *reinterpret_cast<u32x4*>(words + rr * wpr + wc) =
-            *reinterpret_cast<const u32x4*>(&tw[buf][row][q * 4]);
+      if (rr < d_out && wc < wpr) {
+        if (!kRows || vec_words) {
+          *reinterpret_cast<u32x4*>(words + rr * wpr + wc) =
+              *reinterpret_cast<const u32x4*>(&tw[buf][row][q * 4]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (wc + e < wpr) words[rr * wpr + wc + e] = tw[buf][row][q * 4 + e];
+        }
+      }
     } else if (wave == kTileWaves - 1 && tiled) {
       // tiled copy: lane = (4-word group, row); the tile's 8 rows of a group are one line
       const int q = lane >> 3, row = lane & 7;
@@ -179,6 +200,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
     }
   }
 
+  if (kRows) return;
   __shared__ double wsum[kTileWaves];
   acc = wave_sum(acc);
   if (lane == 0) wsum[wave] = acc;
@@ -301,6 +323,18 @@ __global__ __launch_bounds__(kPass2Threads) void compress_pass2(const double* __
   if (threadIdx.x == 0) alpha[0] = (float)(red[0] / n);
 }
 
+// Per-row scales: thread r adds row r's column-group partials in column order.
+constexpr int kRowsPass2Threads = 256;
+__global__ __launch_bounds__(kRowsPass2Threads) void compress_rows_pass2(
+    const double* __restrict__ partials, int64_t d_out, int64_t ncg, double d_in,
+    float* __restrict__ alpha) {
+  const int64_t r = (int64_t)blockIdx.x * kRowsPass2Threads + threadIdx.x;
+  if (r >= d_out) return;
+  double s = 0.0;
+  for (int64_t c = 0; c < ncg; ++c) s += partials[r * ncg + c];
+  alpha[r] = (float)(s / d_in);
+}
+
 int flat_grid(int64_t n) {
   const int64_t n4 = n / 4;
   const int64_t per_block = (int64_t)kThreads * kUnroll;  // float4 per workgroup per sweep
@@ -329,8 +363,8 @@ hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint
   const int grid = tiles ? tile_grid(d_out, d_in) : flat_grid(n);
   clear_stale_error();
   if (tiles)
-    hipLaunchKernelGGL(compress_tiles, dim3(grid), dim3(kTileWaves * 64), 0, stream, delta, d_out,
-                       d_in, words, tiled, partials);
+    hipLaunchKernelGGL(compress_tiles<false>, dim3(grid), dim3(kTileWaves * 64), 0, stream, delta,
+                       d_out, d_in, words, tiled, 1, partials);
   else if (n / 32 < (int64_t(1) << 32))
     hipLaunchKernelGGL(compress_pass1<true>, dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const f32x4*>(delta), n / 4, words, tiled, d_in / 32,
@@ -343,6 +377,27 @@ hipError_t launch_compress(const float* delta, int64_t d_out, int64_t d_in, uint
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(compress_pass2, dim3(1), dim3(kPass2Threads), 0, stream, partials, grid,
                      (double)n, alpha);
+  return hipGetLastError();
+}
+
+int64_t compress_rows_partials(int64_t d_out, int64_t d_in) {
+  return d_out * ((d_in + kTileCols - 1) / kTileCols);
+}
+
+hipError_t launch_compress_rows(const float* delta, int64_t d_out, int64_t d_in, uint32_t* words,
+                                uint32_t* tiled, float* alpha, double* partials,
+                                hipStream_t stream) {
+  const int grid = tile_grid(d_out, d_in);
+  const int vec = d_in % 128 == 0 && reinterpret_cast<uintptr_t>(words) % 16 == 0;
+  clear_stale_error();
+  hipLaunchKernelGGL(compress_tiles<true>, dim3(grid), dim3(kTileWaves * 64), 0, stream, delta,
+                     d_out, d_in, words, tiled, vec, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (d_out + kRowsPass2Threads - 1) / kRowsPass2Threads;
+  hipLaunchKernelGGL(compress_rows_pass2, dim3((unsigned)blocks), dim3(kRowsPass2Threads), 0,
+                     stream, partials, d_out, (d_in + kTileCols - 1) / kTileCols, (double)d_in,
+                     alpha);
   return hipGetLastError();
 }
 

@@ -42,12 +42,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 
   int slot[M];
   bool fresh[M];
-  unsigned abits[M];
 #pragma unroll
   for (int t = 0; t < M; ++t) {
     slot[t] = a.tok_slot[t];
     fresh[t] = (t == 0) || (slot[t] != slot[t - 1]);
-    abits[t] = slot[t] >= 0 ? __float_as_uint(*a.alpha[slot[t]]) : 0u;
   }
 
   const uint16_t* wrow[kRows];
@@ -57,6 +55,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     rowc[r] = min(row0 + r, a.d_out - 1);  // rows past the end read the last row; not stored
     wrow[r] = a.w + (size_t)rowc[r] * d_in;
   }
+  // the scale of each (row, token): the variant's one alpha, or its row's alpha
+  unsigned abits[kRows][M];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int t = 0; t < M; ++t)
+      abits[r][t] = slot[t] >= 0 ? __float_as_uint(a.alpha[slot[t]][((a.alpha_rows >> slot[t]) & 1u)
+                                                                          ? rowc[r]
+                                                                          : 0])
+                                 : 0u;
 
   float acc[kRows][M];
 #pragma unroll
@@ -96,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         float weff = wf;
 #pragma unroll
         for (int t = 0; t < M; ++t) {
-          if (fresh[t]) weff = slot[t] >= 0 ? wf + signed_alpha(abits[t], word[t], pos0 + e) : wf;
+          if (fresh[t]) weff = slot[t] >= 0 ? wf + signed_alpha(abits[r][t], word[t], pos0 + e) : wf;
           acc[r][t] = fmaf(weff, xf[t][e], acc[r][t]);
         }
       }

@@ -118,8 +118,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   const int xrow0 = a.mt_row[mt];
   const int nrows = a.mt_rows[mt];
   const int slot = a.mt_slot[mt];
-  // base-model tiles rebuild with alpha = 0, which leaves every weight as it is
-  const unsigned abits = slot >= 0 ? __float_as_uint(*a.alpha[slot]) & 0x7FFFFFFFu : 0u;
   const int n0 = nt * kPrefillBN;
   const int wpr = d_in >> 5;  // sign words per row
   const int nsteps = d_in / kBK;
@@ -127,6 +125,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
+  // the scale of the two rows the lane rebuilds (32w + 16rt + j): the variant's one alpha or the
+  // row's; base-model tiles rebuild with alpha = 0, which leaves every weight as it is
+  unsigned abits[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int ri = ((a.alpha_rows >> (slot & 31)) & 1u) ? min(n0 + 32 * wave + 16 * rt + j, d_out - 1) : 0;
+    abits[rt] = slot >= 0 ? __float_as_uint(a.alpha[slot][ri]) & 0x7FFFFFFFu : 0u;
+  }
 
   // ---- copies of a pair: wave w moves tokens 32w .. 32w + 31 (4 x 1 KiB) and its own weight rows
   // 32w .. 32w + 31 (4 x 1 KiB), 8 rows of 128 bytes per copy: lane L fills stored unit L % 8 of
@@ -193,8 +199,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
     const unsigned char* pb = smem + (unsigned)((s >> 1) & 1) * kPair;
     const u32x4 w0 = *reinterpret_cast<const u32x4*>(pb + a_lane[h]);
     const u32x4 w1 = *reinterpret_cast<const u32x4*>(pb + a_lane[h] + 16 * 128);
-    const u32x4 A0 = rebuild8(w0, ~sw[0][s & 3], 8u * g, abits, one_lo, one_hi);
-    const u32x4 A1 = rebuild8(w1, ~sw[1][s & 3], 8u * g, abits, one_lo, one_hi);
+    const u32x4 A0 = rebuild8(w0, ~sw[0][s & 3], 8u * g, abits[0], one_lo, one_hi);
+    const u32x4 A1 = rebuild8(w1, ~sw[1][s & 3], 8u * g, abits[1], one_lo, one_hi);
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       const u32x4 B = *reinterpret_cast<const u32x4*>(pb + b_lane[h] + tt * 16 * 128);

@@ -254,7 +254,9 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(const StreamArgs a)
     const int ti = wave * NTW + i;
     if (ti < T) {
       const int s = a.tile_slot[ti];
-      const float al = s >= 0 ? *a.prob[p].alpha[s] : 0.f;
+      const float* ap = s >= 0 ? a.prob[p].alpha[s] : nullptr;
+      const bool per_row = s >= 0 && ((a.prob[p].alpha_rows >> s) & 1u);
+      const float al = s >= 0 ? ap[0] : 0.f;
       if (j < (int)a.tile_valid[ti]) {
         const size_t ybase = (size_t)(a.tile_src[ti] + j) * d_out;
 #pragma unroll
@@ -262,7 +264,10 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(const StreamArgs a)
           const int orow = row0 + rt * 16 + 4 * g;
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = accb[i][rt][r] + al * accd[i][rt][r];
+          for (int r = 0; r < 4; ++r) {
+            const float ar = per_row ? ap[min(orow + r, d_out - 1)] : al;
+            v[r] = accb[i][rt][r] + ar * accd[i][rt][r];
+          }
           if (a.y_f32) {
             float* y = reinterpret_cast<float*>(a.prob[p].y) + ybase;
 #pragma unroll

@@ -52,7 +52,8 @@ def oracle_delta_term(x, variants, seg_offsets, seg_variant, d_out, d_in):
             continue
         words, alpha = variants[v]
         sgn = O.unpack_signs_ref(words, d_in).astype(np.float64)
-        y[lo:hi] = np.float64(np.float32(alpha)) * (x[lo:hi] @ sgn.T)
+        a = np.asarray(alpha, dtype=np.float32).astype(np.float64)  # scalar or one per row
+        y[lo:hi] = (x[lo:hi] @ sgn.T) * (a if a.ndim == 0 else a[None, :])
     return y
 
 

@@ -37,7 +37,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.abi_version() == 4
+    assert bd.abi_version() == 5
     for s in range(7):
         assert L.bitdelta_status_string(s)
     assert L.bitdelta_status_string(99) == b"unknown status"
@@ -119,6 +119,48 @@ def test_compress_from_weights_validation():
     assert _compress_pair(FAKE, FAKE, 64, 96, FAKE, FAKE, FAKE, ws, tiled=FAKE) == SHAPE
     # the row-tile form serves every d_in: its partials fit the compress workspace
     assert bd.compress_workspace_bytes(64, 96) >= 8 * ((64 + 7) // 8)
+
+
+def _compress_rows(delta, d_out, d_in, words, alpha, ws, ws_bytes, tiled=None):
+    return L.bitdelta_compress_rows(delta, d_out, d_in, words, tiled, alpha, ws, ws_bytes, None)
+
+
+def test_compress_rows_validation():
+    ws = bd.compress_rows_workspace_bytes(64, 96)
+    assert ws == 64 * 1 * 8  # one fp64 partial per row and 1024-column group
+    assert bd.compress_rows_workspace_bytes(10, 2080) == 10 * 3 * 8
+    assert bd.compress_rows_workspace_bytes(0, 96) == 0 and bd.compress_rows_workspace_bytes(4, 48) == 0
+    assert _compress_rows(None, 64, 96, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress_rows(FAKE, 64, 96, None, FAKE, FAKE, ws) == INVALID
+    assert _compress_rows(FAKE, 64, 96, FAKE, None, FAKE, ws) == INVALID
+    assert _compress_rows(FAKE, 0, 96, FAKE, FAKE, FAKE, ws) == INVALID
+    assert _compress_rows(FAKE, 64, 48, FAKE, FAKE, FAKE, ws) == SHAPE
+    assert _compress_rows(FAKE + 8, 64, 96, FAKE, FAKE, FAKE, ws) == ALIGN
+    assert _compress_rows(FAKE, 64, 96, FAKE + 2, FAKE, FAKE, ws) == ALIGN
+    assert _compress_rows(FAKE, 64, 96, FAKE, FAKE + 2, FAKE, ws) == ALIGN
+    assert _compress_rows(FAKE, 64, 96, FAKE, FAKE, FAKE + 4, ws) == ALIGN
+    assert _compress_rows(FAKE, 64, 96, FAKE, FAKE, FAKE, ws - 8) == WORKSPACE
+    assert _compress_rows(FAKE, 64, 96, FAKE, FAKE, FAKE, ws, tiled=FAKE) == SHAPE
+    assert _compress_rows(FAKE, 64, 128, FAKE, FAKE, FAKE, ws, tiled=FAKE + 8) == ALIGN
+
+
+def test_alpha_per_row_flag_validation():
+    """alpha_per_row must be 0 or 1; a forced split launch refuses per-row variants (it folds the
+    scale into the activations), before anything is enqueued."""
+    o = np.array([0, 8], dtype=np.int32)
+    v = np.array([0], dtype=np.int32)
+    op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    vp = v.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    varr = (bd._Variant * 1)()
+    varr[0].sign_words, varr[0].sign_words_t128, varr[0].alpha = FAKE, FAKE, FAKE
+    prob = (bd._Problem * 1)()
+    prob[0].x, prob[0].w_base, prob[0].y = FAKE, FAKE, FAKE
+    prob[0].d_out, prob[0].d_in = 256, 256
+    prob[0].variants = ctypes.cast(varr, ctypes.POINTER(bd._Variant))
+    prob[0].num_variants = 1
+    for flag, path, want in [(2, 0, INVALID), (-1, 0, INVALID), (1, 4, UNSUPPORTED)]:
+        varr[0].alpha_per_row = flag
+        assert L.bitdelta_matmul_grouped(prob, 1, 8, op, vp, 1, 0, path, FAKE, 1 << 40, None) == want
 
 
 def _matmul(x, w, m, d_out, d_in, variants, offs, segv, y, y_dtype=0, path=None, ws=FAKE,
