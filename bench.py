@@ -201,6 +201,31 @@ def measure_compress_pair(torch, bd, reps=5):
     return {"shape": [d_out, d_in], "ms": ms, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
+def measure_compress_rows(torch, bd, reps=5):
+    """Compress with one alpha per output row at the gate / up shape (28672 x 8192).
+    Algorithmic bytes: Delta read (4 B per element), the row-major words and the tiled copy
+    written (n / 8 each) and the d_out alphas."""
+    d_out, d_in = 28672, 8192
+    delta = WL.gpu_laplace_f32(torch, (d_out, d_in), 3e-4, WL.substream_seed(6, 0, "gate", 0, "delta"))
+    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    alpha = torch.empty(d_out, dtype=torch.float32, device="cuda")
+    tiled = torch.empty(bd.sign_words_t128(d_out, d_in), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(bd.compress_rows_workspace_bytes(d_out, d_in), 8) // 8,
+                     dtype=torch.float64, device="cuda")
+    for _ in range(2):
+        bd.compress_rows(delta, words, alpha, workspace=ws, tiled=tiled)
+    t = EventTimer(torch, reserve=reps)
+    n = d_out * d_in
+    for _ in range(reps):
+        t.start()
+        bd.compress_rows(delta, words, alpha, workspace=ws, tiled=tiled)
+        t.stop(4 * n + 2 * (n // 8) + 4 * d_out)
+    ms = t.total_ms() / reps
+    gbs = t.bytes / reps / (ms / 1e3) / 1e9
+    del delta, words, tiled, ws
+    return {"shape": [d_out, d_in], "ms": ms, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
 def decode_bytes(blk, m, n_active):
     tot = 0
     for L in blk:
@@ -308,6 +333,7 @@ def run_decode(args, torch, bd, config):
     path = bd.auto_path(m, offs, segv) if args.path == "auto" else bd.PATHS[args.path]
     # compress from a weight pair, after the timed region (default workload only)
     pair = measure_compress_pair(torch, bd) if config == 5 else None
+    rows = measure_compress_rows(torch, bd) if config == 5 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,6 +370,7 @@ def run_decode(args, torch, bd, config):
                      "gbs": comp_bytes / (comp_ms / 1e3) / 1e9,
                      "frac": comp_bytes / (comp_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "compress_from_weights": pair,
+        "compress_rows": rows,
         "cpu_baseline": cpu,
     }
 
