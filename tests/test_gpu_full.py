@@ -178,6 +178,29 @@ def test_full_size_prefill_sampled():
         _check_rows(got32, ref, delta_term, 5e-3, 0.75, ("f32", int(v)))
 
 
+def test_full_size_compress_rows():
+    """Per-row alphas at the down-projection shape (8192 x 28672, 28 column groups per row):
+    every sign word against the oracle, and the alpha of 64 sampled rows (the first, the last
+    and 62 seeded ones) against the oracle's exact row mean."""
+    d_out, d_in = 8192, 28672
+    delta = WL.gpu_laplace_f32(torch, (d_out, d_in), 3e-4, WL.substream_seed(6, 0, "down", 0, "delta"))
+    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    alpha = torch.empty(d_out, dtype=torch.float32, device="cuda")
+    tiled = torch.empty(bd.sign_words_t128(d_out, d_in), dtype=torch.int32, device="cuda")
+    bd.compress_rows(delta, words, alpha, tiled=tiled)
+    torch.cuda.synchronize()
+    d_host = delta.cpu().numpy()
+    ref_words = O.pack_signs_ref(O.signs_ref(d_host))
+    np.testing.assert_array_equal(words.cpu().numpy().view(np.uint32), ref_words)
+    rows = np.unique(np.concatenate([[0, d_out - 1],
+                                     np.random.default_rng(80).integers(0, d_out, size=62)]))
+    ref_a = O.alpha_rows_ref(d_host[rows]).astype(np.float64)
+    got_a = alpha.cpu().numpy()[rows].astype(np.float64)
+    assert np.all(np.abs(got_a - ref_a) <= 1e-6 * ref_a)
+    got_t = tiled.cpu().numpy().view(np.uint32).reshape(-1, 512)
+    np.testing.assert_array_equal(got_t[0].reshape(128, 4), ref_words[:128, :4])
+
+
 def test_full_size_compress_from_weights():
     """Compress from a (fine-tuned, base) bf16 pair at a 70B shape (8192 x 8192, the q / o
     projection): every sign word and alpha against the oracle's task vector."""
