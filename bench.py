@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--path", default="auto", choices=("auto", "gemv", "stream", "split", "prefill"),
                    help="decode kernel family (auto: what the library picks)")
+    p.add_argument("--alpha-rows", action="store_true",
+                   help="decode configs: compress every variant with one alpha per output row "
+                        "(the library then runs 5-256 token batches on the streaming kernel)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB device buffer three times (a plain copy kernel of known "
                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -109,11 +112,13 @@ class Linear:
         self.y = None
 
 
-def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nvar=NUM_VARIANTS):
+def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nvar=NUM_VARIANTS,
+                 alpha_rows=False):
     dev = "cuda"
     maxn = max(d_out * d_in for _, d_out, d_in in linears)
     dbuf = torch.empty(maxn, dtype=torch.float32, device=dev)
-    ws_bytes = max(bd.compress_workspace_bytes(d_out, d_in) for _, d_out, d_in in linears)
+    ws_bytes = max(max(bd.compress_workspace_bytes(d_out, d_in),
+                       bd.compress_rows_workspace_bytes(d_out, d_in)) for _, d_out, d_in in linears)
     ws = torch.empty(max(ws_bytes, 8) // 8, dtype=torch.float64, device=dev)
     layers = []
     for b in range(blocks):
@@ -126,13 +131,17 @@ def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nva
                                            WL.substream_seed(config, b, name, v, "delta"),
                                            out=dbuf[:d_out * d_in])
                 words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device=dev)
-                alpha = torch.empty(1, dtype=torch.float32, device=dev)
+                alpha = torch.empty(d_out if alpha_rows else 1, dtype=torch.float32, device=dev)
                 nt = bd.sign_words_t128(d_out, d_in)
                 tiled = torch.empty(nt, dtype=torch.int32, device=dev) if nt > 0 else None
                 compress_timer.start()
-                bd.compress(delta, words, alpha, workspace=ws, tiled=tiled)
+                if alpha_rows:
+                    bd.compress_rows(delta, words, alpha, workspace=ws, tiled=tiled)
+                else:
+                    bd.compress(delta, words, alpha, workspace=ws, tiled=tiled)
                 # reads Delta once, writes the row-major words, the tiled copy and alpha
-                compress_timer.stop(4 * d_out * d_in + (2 if nt > 0 else 1) * (d_out * d_in // 8) + 4)
+                compress_timer.stop(4 * d_out * d_in + (2 if nt > 0 else 1) * (d_out * d_in // 8) +
+                                    4 * alpha.numel())
                 L.variants.append((words, alpha, tiled))
             blk.append(L)
         layers.append(blk)
@@ -226,11 +235,12 @@ def measure_compress_rows(torch, bd, reps=5):
     return {"shape": [d_out, d_in], "ms": ms, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
-def decode_bytes(blk, m, n_active):
+def decode_bytes(blk, m, n_active, alpha_rows=False):
     tot = 0
     for L in blk:
         n = L.d_out * L.d_in
-        tot += 2 * n + n_active * (n // 8 + 4) + 2 * m * L.d_in + 2 * m * L.d_out
+        tot += (2 * n + n_active * (n // 8 + 4 * (L.d_out if alpha_rows else 1)) + 2 * m * L.d_in +
+                2 * m * L.d_out)
     return tot
 
 
@@ -291,7 +301,8 @@ def run_decode(args, torch, bd, config):
     log(f"[setup] config {config}: {blocks} block(s), M={m}, segments={list(np.diff(offs))}")
 
     comp = EventTimer(torch)
-    layers = build_layers(torch, bd, config, blocks, linears, scales, comp, nvar)
+    layers = build_layers(torch, bd, config, blocks, linears, scales, comp, nvar,
+                          alpha_rows=args.alpha_rows)
     comp_ms = comp.total_ms()
     for b, blk in enumerate(layers):
         for L in blk:
@@ -326,11 +337,13 @@ def run_decode(args, torch, bd, config):
     ms_step = (t1 - t0) * 1e3 / args.steps
     kern_ms = kt.total_ms()
     launches = len(kt.pairs)
-    bytes_launch = decode_bytes(layers[0], m, n_active)  # every block has the same shapes
+    bytes_launch = decode_bytes(layers[0], m, n_active, args.alpha_rows)  # every block has the same shapes
     avg_launch_s = kern_ms / launches / 1e3
     achieved = bytes_launch / avg_launch_s / 1e9
     total_elems = sum(L.d_out * L.d_in for blk in layers for L in blk)
     path = bd.auto_path(m, offs, segv) if args.path == "auto" else bd.PATHS[args.path]
+    if args.alpha_rows and path == 4:
+        path = 2  # per-row scales: the library runs the batch on the streaming kernel
     # compress from a weight pair, after the timed region (default workload only)
     pair = measure_compress_pair(torch, bd) if config == 5 else None
     rows = measure_compress_rows(torch, bd) if config == 5 else None
@@ -354,7 +367,8 @@ def run_decode(args, torch, bd, config):
         "dtype": {1: "bf16 in, fp32 arithmetic", 2: "bf16 MFMA (fp32 accumulate)",
                   4: "bf16 MFMA + fp4 x fp6 MFMA (fp32 accumulate)"}.get(path, "bf16"),
         "data": "synthetic (seeded; random weights/deltas)",
-        "config": {"workload": names[config], "config_index": config, "tokens_per_step": m,
+        "config": {"workload": names[config] + (", one alpha per output row" if args.alpha_rows else ""),
+                   "config_index": config, "tokens_per_step": m,
                    "segments": [int(v) for v in np.diff(offs)], "active_variants": n_active,
                    "launches_per_step": launches // args.steps,
                    "kernel_path": {1: "gemv", 2: "stream", 3: "prefill", 4: "split"}[path],
