@@ -269,8 +269,10 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
                                         int32_t y_dtype, int32_t path, void* workspace,
                                         size_t workspace_bytes, bitdelta_stream stream);
 
-/* The kernel family bitdelta_matmul_grouped's AUTO would pick for this batch (a
- * bitdelta_path value), or -1 for invalid segments.  Host only. */
+/* The kernel family bitdelta_matmul_grouped's AUTO picks for this batch shape (a bitdelta_path
+ * value), or -1 for invalid segments.  Host only.  It sees the shape, not the variants: where it
+ * answers SPLIT, a call whose variants lack the tiled sign words or d_in % 128, or that holds a
+ * per-row-alpha variant, runs STREAM instead (PREFILL when streaming does not apply either). */
 int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t* seg_variant,
                            int32_t num_segments);
 
