@@ -1,0 +1,82 @@
+"""Delta cache policy: the oracle pinned by a hand-derived trace and by invariants over random
+traces, then the library's C++ manager against the oracle, decision by decision."""
+import numpy as np
+import pytest
+
+import oracle.residency_oracle as R
+
+
+def test_oracle_hand_trace():
+    # 4 variants of 10 bytes, room for 3, the top 1 pinned
+    c = R.ResidencyRef([10, 10, 10, 10], 30, num_pinned=1)
+    assert c.request(0) == (R.LOAD, [])           # cold start
+    assert c.request(0) == (R.QUEUED, [])         # waits for the load in flight
+    c.load_done(0)
+    assert c.request(0) == (R.HIT, [])            # variant 0: 3 requests, pinned
+    assert c.request(1) == (R.LOAD, [])
+    c.load_done(1)
+    assert c.request(2) == (R.LOAD, [])
+    c.load_done(2)
+    assert c.request(1) == (R.HIT, [])            # 1 is now more recent than 2
+    assert c.request(3) == (R.LOAD, [2])          # full: the least recent unpinned goes
+    assert c.state == [R.RESIDENT, R.RESIDENT, R.ABSENT, R.LOADING]
+    assert c.request(2) == (R.LOAD, [1])          # 3 is loading, 0 pinned: only 1 can go
+    assert c.request(1) == (R.NO_ROOM, [])        # 0 pinned, 2 and 3 loading: nothing to evict
+    assert c.state == [R.RESIDENT, R.ABSENT, R.LOADING, R.LOADING]
+    c.load_done(3)
+    c.load_done(2)
+    # counts now 0:3, 1:3, 2:2, 3:1: the pinned one is 0 (tie with 1 goes to the smaller id)
+    assert c.pinned() == {0}
+    # this request makes 1 the most requested (4 against 3): 1 is pinned now, and 0, the least
+    # recent of the others (time 3, against 7 for 3 and 8 for 2), is evicted
+    assert c.request(1) == (R.LOAD, [0])
+    assert c.pinned() == {1}
+    with pytest.raises(ValueError):
+        c.load_done(0)
+
+
+def test_oracle_pins_follow_traffic():
+    c = R.ResidencyRef([5] * 6, 10, num_pinned=2)
+    for v in (4, 4, 4, 2, 2, 5):
+        c.request(v)
+        if c.state[v] == R.LOADING:
+            c.load_done(v)
+    assert c.pinned() == {4, 2}
+    # 4 and 2 are resident and pinned, so 5 cannot be loaded and any other request finds no room
+    assert c.state[4] == R.RESIDENT and c.state[2] == R.RESIDENT and c.state[5] == R.ABSENT
+    assert c.request(0) == (R.NO_ROOM, [])
+
+
+def _random_trace(seed, n, steps):
+    rng = np.random.default_rng(seed)
+    p = 1.0 / np.arange(1, n + 1) ** 1.1
+    return rng.choice(n, size=steps, p=p / p.sum()), rng.random(steps)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_oracle_invariants(seed):
+    n = 14
+    sizes = np.random.default_rng(100 + seed).integers(1, 9, size=n) * 1000
+    cap = int(sizes.sum() * 0.6)
+    c = R.ResidencyRef(sizes, cap, num_pinned=6)
+    trace, coin = _random_trace(seed, n, 3000)
+    for v, u in zip(trace, coin):
+        state_before = list(c.state)
+        act, ev = c.request(int(v))
+        pins = c.pinned()  # the pinned set counts the request itself
+        assert c.used() <= cap
+        for e in ev:  # only resident, unpinned, other variants are evicted
+            assert state_before[e] == R.RESIDENT and e not in pins and e != v
+        if act == R.NO_ROOM:
+            assert c.state == state_before
+        if u < 0.7:  # loads finish at random later points
+            for w in range(n):
+                if c.state[w] == R.LOADING:
+                    c.load_done(w)
+    # with room for the pinned set, the top variants by traffic end up resident
+    top = sorted(range(n), key=lambda v: (-c.count[v], v))[:6]
+    for v in top:
+        if c.state[v] == R.ABSENT:
+            c.request(v)
+            c.load_done(v)
+        assert c.state[v] != R.ABSENT
