@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define BITDELTA_ABI_VERSION 5
+#define BITDELTA_ABI_VERSION 6
 #define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
 #define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
 #define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
@@ -275,6 +275,46 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
  * per-row-alpha variant, runs STREAM instead (PREFILL when streaming does not apply either). */
 int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t* seg_variant,
                            int32_t num_segments);
+
+/* ---- Delta residency (host only, ABI 6) -------------------------------------------------
+ * Which variants' compressed deltas (sign words and alpha) stay in device memory, after the
+ * BitDelta post, "Infrastructure details": the variants with the most requests stay pinned (the
+ * top few by volume always resident), the rest share the remaining capacity with least-recently-
+ * used eviction; a request for a variant that is not resident starts a load; requests for a
+ * variant whose load is in flight wait for it rather than starting another.  Request rate is the
+ * count of requests so far; pinned = the num_pinned highest counts (ties to the smaller id) among
+ * variants requested at least once, the current request included.  Pinned and loading variants
+ * are never evicted; eviction takes the least recently requested variant first (ties to the
+ * smaller id) until the new delta fits.  The caller moves the bytes and calls load_done.
+ * Each call locks the manager, so calls from several threads are serialised. */
+typedef struct bitdelta_residency bitdelta_residency;
+
+enum {
+  BITDELTA_RESIDENCY_HIT = 0,     /* resident: serve now                                      */
+  BITDELTA_RESIDENCY_LOAD = 1,    /* start loading it (after dropping the evicted variants)   */
+  BITDELTA_RESIDENCY_QUEUED = 2,  /* its load is in flight: wait for that load                 */
+  BITDELTA_RESIDENCY_NO_ROOM = 3  /* cannot fit now (the rest is pinned or loading); nothing
+                                   * changed but the request counts                           */
+};
+enum { BITDELTA_VARIANT_ABSENT = 0, BITDELTA_VARIANT_LOADING = 1, BITDELTA_VARIANT_RESIDENT = 2 };
+
+/* num_variants in 1..4096; variant_bytes [host] num_variants sizes > 0 (copied); capacity_bytes
+ * > 0; num_pinned >= 0.  *out receives the manager (NULL on error).  Errors: INVALID_ARG. */
+bitdelta_status bitdelta_residency_create(int32_t num_variants, const int64_t* variant_bytes,
+                                          int64_t capacity_bytes, int32_t num_pinned,
+                                          bitdelta_residency** out);
+void bitdelta_residency_destroy(bitdelta_residency* r);
+/* One request for `variant`: *action = BITDELTA_RESIDENCY_*; evicted [host] room for
+ * num_variants ids receives the variants dropped, in eviction order, *num_evicted their count.
+ * Errors: INVALID_ARG (null pointer, variant out of range). */
+bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t variant, int32_t* action,
+                                           int32_t* evicted, int32_t* num_evicted);
+/* The load of `variant` has finished: it becomes resident.  INVALID_ARG unless it was loading. */
+bitdelta_status bitdelta_residency_load_done(bitdelta_residency* r, int32_t variant);
+/* BITDELTA_VARIANT_* of `variant`, or -1 for a bad argument. */
+int32_t bitdelta_residency_state(bitdelta_residency* r, int32_t variant);
+/* Bytes held by resident and loading variants, or -1 for a null manager. */
+int64_t bitdelta_residency_used_bytes(bitdelta_residency* r);
 
 #ifdef __cplusplus
 }

@@ -89,6 +89,21 @@ def _lib():
                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.bitdelta_compress_rows_workspace_bytes.restype = ctypes.c_size_t
         L.bitdelta_compress_rows_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.bitdelta_residency_create.restype = ctypes.c_int
+        L.bitdelta_residency_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                                ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.POINTER(ctypes.c_void_p)]
+        L.bitdelta_residency_destroy.restype = None
+        L.bitdelta_residency_destroy.argtypes = [ctypes.c_void_p]
+        L.bitdelta_residency_request.restype = ctypes.c_int
+        L.bitdelta_residency_request.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p,
+                                                 _i32p]
+        L.bitdelta_residency_load_done.restype = ctypes.c_int
+        L.bitdelta_residency_load_done.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+        L.bitdelta_residency_state.restype = ctypes.c_int32
+        L.bitdelta_residency_state.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+        L.bitdelta_residency_used_bytes.restype = ctypes.c_int64
+        L.bitdelta_residency_used_bytes.argtypes = [ctypes.c_void_p]
         L.bitdelta_sign_words_t128.restype = ctypes.c_int64
         L.bitdelta_sign_words_t128.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.bitdelta_plan_segments.restype = ctypes.c_int
@@ -344,3 +359,43 @@ def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf1
         _dev(y, "torch.bfloat16" if out_dtype == "bf16" else "torch.float32", "y"),
         _OUT[out_dtype], ws_ptr, ws_bytes, _stream(stream)), "bitdelta_matmul")
     return y
+
+
+class Residency:
+    """The library's delta residency manager (host only): request(v) -> (action, evicted ids),
+    with action one of HIT, LOAD, QUEUED, NO_ROOM; load_done(v) when a load has finished."""
+    HIT, LOAD, QUEUED, NO_ROOM = 0, 1, 2, 3
+    ABSENT, LOADING, RESIDENT = 0, 1, 2
+
+    def __init__(self, variant_bytes, capacity_bytes: int, num_pinned: int = 6):
+        L = _lib()
+        self._n = len(variant_bytes)
+        sizes = (ctypes.c_int64 * max(self._n, 1))(*[int(b) for b in variant_bytes])
+        h = ctypes.c_void_p()
+        _check(L.bitdelta_residency_create(self._n, sizes, int(capacity_bytes), int(num_pinned),
+                                           ctypes.byref(h)), "bitdelta_residency_create")
+        self._h = h
+        self._ev = (ctypes.c_int32 * self._n)()
+        self._act = ctypes.c_int32()
+        self._ne = ctypes.c_int32()
+
+    def request(self, v: int):
+        _check(_lib().bitdelta_residency_request(self._h, int(v), ctypes.byref(self._act), self._ev,
+                                                 ctypes.byref(self._ne)),
+               "bitdelta_residency_request")
+        return self._act.value, [self._ev[i] for i in range(self._ne.value)]
+
+    def load_done(self, v: int):
+        _check(_lib().bitdelta_residency_load_done(self._h, int(v)), "bitdelta_residency_load_done")
+
+    def state(self, v: int) -> int:
+        return int(_lib().bitdelta_residency_state(self._h, int(v)))
+
+    def used_bytes(self) -> int:
+        return int(_lib().bitdelta_residency_used_bytes(self._h))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _LIB is not None:
+            _LIB.bitdelta_residency_destroy(h)
+            self._h = None

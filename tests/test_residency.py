@@ -80,3 +80,48 @@ def test_oracle_invariants(seed):
             c.request(v)
             c.load_done(v)
         assert c.state[v] != R.ABSENT
+
+
+bd = pytest.importorskip("tenant_serving_bitdelta_amd")
+
+
+@pytest.mark.parametrize("seed,n,pinned,frac", [(0, 14, 6, 0.6), (1, 14, 6, 0.45), (2, 5, 1, 0.5),
+                                                (3, 64, 6, 0.3), (4, 14, 0, 0.5), (5, 3, 6, 0.9)])
+def test_manager_matches_oracle(seed, n, pinned, frac):
+    rng = np.random.default_rng(200 + seed)
+    sizes = [int(s) for s in rng.integers(1, 9, size=n) * 1_000_000_007]  # > 2^32 in total
+    cap = max(int(sum(sizes) * frac), max(sizes))
+    ref = R.ResidencyRef(sizes, cap, num_pinned=pinned)
+    lib = bd.Residency(sizes, cap, num_pinned=pinned)
+    trace, coin = _random_trace(seed, n, 4000)
+    for step, (v, u) in enumerate(zip(trace, coin)):
+        got, want = lib.request(int(v)), ref.request(int(v))
+        assert got == (want[0], want[1]), (step, got, want)
+        # a random subset of the loads in flight finishes
+        for w in range(n):
+            if ref.state[w] == R.LOADING and rng.random() < u:
+                ref.load_done(w)
+                lib.load_done(w)
+        assert [lib.state(w) for w in range(n)] == ref.state, step
+        assert lib.used_bytes() == ref.used()
+
+
+def test_manager_argument_errors():
+    with pytest.raises(bd.BitDeltaError):
+        bd.Residency([], 10)
+    with pytest.raises(bd.BitDeltaError):
+        bd.Residency([10, 0], 10)
+    with pytest.raises(bd.BitDeltaError):
+        bd.Residency([10], 0)
+    with pytest.raises(bd.BitDeltaError):
+        bd.Residency([10], 10, num_pinned=-1)
+    r = bd.Residency([10, 10], 10)
+    with pytest.raises(bd.BitDeltaError):
+        r.request(2)
+    with pytest.raises(bd.BitDeltaError):
+        r.load_done(0)  # not loading
+    assert r.state(5) == -1
+    assert r.request(0) == (bd.Residency.LOAD, [])
+    assert r.request(1) == (bd.Residency.NO_ROOM, [])  # 0 is loading and cannot be evicted
+    r.load_done(0)
+    assert r.request(1) == (bd.Residency.NO_ROOM, [])  # 0 pinned (num_pinned 6)
