@@ -235,6 +235,32 @@ def measure_compress_rows(torch, bd, reps=5):
     return {"shape": [d_out, d_in], "ms": ms, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
+def measure_delta_upload(torch, reps=3):
+    """Host -> device upload of compressed delta bytes from pinned host memory, what a cold
+    start of a variant moves: 1 GiB copies timed with HIP events on torch's stream, and the time
+    this gives for one 70B variant (80 decoder blocks of q, k, v, o, gate, up, down: the row-major
+    sign words and one alpha per matrix)."""
+    nbytes = 1 << 30
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dev.copy_(host, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dev.copy_(host, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = nbytes / (ms / 1e3) / 1e9
+    shapes = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192),
+              (28672, 8192), (8192, 28672)]
+    variant = 80 * sum(d_out * d_in // 8 + 4 for d_out, d_in in shapes)
+    del host, dev
+    return {"source": "pinned host memory over PCIe", "bytes_per_copy": nbytes, "gbs": gbs,
+            "variant_bytes_70b": variant, "variant_ms": variant / (gbs * 1e9) * 1e3}
+
+
 def decode_bytes(blk, m, n_active, alpha_rows=False):
     tot = 0
     for L in blk:
@@ -347,6 +373,7 @@ def run_decode(args, torch, bd, config):
     # compress from a weight pair, after the timed region (default workload only)
     pair = measure_compress_pair(torch, bd) if config == 5 else None
     rows = measure_compress_rows(torch, bd) if config == 5 else None
+    upload = measure_delta_upload(torch) if config == 5 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -385,6 +412,7 @@ def run_decode(args, torch, bd, config):
                      "frac": comp_bytes / (comp_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "compress_from_weights": pair,
         "compress_rows": rows,
+        "delta_upload": upload,
         "cpu_baseline": cpu,
     }
 
