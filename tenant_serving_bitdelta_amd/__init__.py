@@ -375,15 +375,14 @@ class Residency:
         _check(L.bitdelta_residency_create(self._n, sizes, int(capacity_bytes), int(num_pinned),
                                            ctypes.byref(h)), "bitdelta_residency_create")
         self._h = h
-        self._ev = (ctypes.c_int32 * self._n)()
-        self._act = ctypes.c_int32()
-        self._ne = ctypes.c_int32()
 
     def request(self, v: int):
-        _check(_lib().bitdelta_residency_request(self._h, int(v), ctypes.byref(self._act), self._ev,
-                                                 ctypes.byref(self._ne)),
-               "bitdelta_residency_request")
-        return self._act.value, [self._ev[i] for i in range(self._ne.value)]
+        # output buffers per call, so that threads sharing a manager never read each other's
+        ev = (ctypes.c_int32 * self._n)()
+        act, ne = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib().bitdelta_residency_request(self._h, int(v), ctypes.byref(act), ev,
+                                                 ctypes.byref(ne)), "bitdelta_residency_request")
+        return act.value, [ev[i] for i in range(ne.value)]
 
     def load_done(self, v: int):
         _check(_lib().bitdelta_residency_load_done(self._h, int(v)), "bitdelta_residency_load_done")

@@ -125,3 +125,44 @@ def test_manager_argument_errors():
     assert r.request(1) == (bd.Residency.NO_ROOM, [])  # 0 is loading and cannot be evicted
     r.load_done(0)
     assert r.request(1) == (bd.Residency.NO_ROOM, [])  # 0 pinned (num_pinned 6)
+
+
+def test_manager_concurrent_requests():
+    """Eight threads request and finish loads at once: every load is started exactly once per
+    absence (no double loads), the bytes held never exceed the capacity, and the final states
+    agree with the loads still open."""
+    import threading
+    n, cap = 14, 40
+    sizes = [5] * n
+    r = bd.Residency(sizes, cap, num_pinned=6)
+    lock = threading.Lock()
+    loading = set()
+    errors = []
+
+    def worker(seed):
+        rng = np.random.default_rng(seed)
+        p = 1.0 / np.arange(1, n + 1) ** 1.1
+        for v in rng.choice(n, size=2000, p=p / p.sum()):
+            act, _ = r.request(int(v))
+            if act == bd.Residency.LOAD:
+                with lock:
+                    if int(v) in loading:
+                        errors.append(("double load", int(v)))
+                    loading.add(int(v))
+            if r.used_bytes() > cap:
+                errors.append(("over capacity", r.used_bytes()))
+            if rng.random() < 0.5:
+                with lock:
+                    done = list(loading)
+                    loading.clear()
+                for w in done:
+                    r.load_done(w)
+
+    threads = [threading.Thread(target=worker, args=(300 + i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
+    for w in range(n):
+        assert (r.state(w) == bd.Residency.LOADING) == (w in loading)
