@@ -38,7 +38,8 @@ import math
 import numpy as np
 
 # Above this many elements the alpha sum uses numpy's pairwise fp64 summation (relative error
-# <= ~log2(n) * 2^-53, far below the 1e-6 tolerance) instead of the exact math.fsum.
+# <= ~log2(n) * 2^-53, far below the 1e-6 tolerance) instead of the exact math.fsum.  That branch
+# is pinned separately, at n = 2^23, by closed forms whose fp64 partial sums are all exact.
 FSUM_MAX = 1 << 22
 
 

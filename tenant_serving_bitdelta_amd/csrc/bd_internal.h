@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -29,6 +31,39 @@ __device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
 // of the same thread (another library's query, say), so each launcher clears it first and the
 // check after the launch reports that launch alone.
 inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// ---------------------------------------------------------------------------------------------
+// Per-device one-time set-up, safe when several host threads launch at once: one bit per
+// device id (ids below 64) in an atomic mask.  Setting a kernel attribute twice is harmless, so
+// two threads that both find the bit clear may both set it; neither sees a torn value.
+// ---------------------------------------------------------------------------------------------
+struct DeviceOnce {
+  std::atomic<unsigned long long> done{0};
+};
+// hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes) once per device.
+inline hipError_t set_dynamic_lds_once(DeviceOnce& once, const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit && (once.done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  if (bit) once.done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
+// A device attribute of the current device, queried once per device and kept in `cache`
+// (64 entries, 0 = not queried yet); `fallback` when the query fails or gives a value below 1.
+inline int device_attribute_cached(std::atomic<int>* cache, hipDeviceAttribute_t attr,
+                                   int fallback) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fallback;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v != 0) return v;
+  if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v < 1) v = fallback;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Compress (two passes)

@@ -294,13 +294,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   for (int m = 0; m < a.n_mtiles; ++m)
     if (a.mt_rows[m] < 1 || a.mt_rows[m] > kPrefillBM) return hipErrorInvalidValue;
-  static bool configured = false;  // benign race: every caller sets the same value
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static DeviceOnce once;
+  hipError_t e = set_dynamic_lds_once(once, reinterpret_cast<const void*>(&prefill_kernel), (int)kLds);
+  if (e != hipSuccess) return e;
   // grid: 8 XCD lists of whole 32-tile groups
   const int ngroups = ((a.n_mtiles + kGroupM - 1) / kGroupM) * ((a.n_ntiles + kGroupN - 1) / kGroupN);
   const int nblocks = ((ngroups + 7) / 8) * 8 * kGroupM * kGroupN;

@@ -632,28 +632,18 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
 
 // Dynamic LDS one workgroup may use on the current device, capped at one compute unit's.
 int lds_limit() {
-  static int cached[64];  // per device, 0 = not queried yet (benign race: same value)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      return 0;
-    cached[dev] = v < (int)kLdsCap ? v : (int)kLdsCap;
-  }
-  return cached[dev];
+  static std::atomic<int> cached[64];  // per device, 0 = not queried yet
+  const int v = device_attribute_cached(cached, hipDeviceAttributeMaxSharedMemoryPerBlock, 0);
+  return v < (int)kLdsCap ? v : (int)kLdsCap;
 }
 
 template <int ND, int NG>
 hipError_t launch_nd_ng(const SplitArgs& a, int nblocks, unsigned stage, int nst,
                          hipStream_t stream) {
-  static bool configured = false;  // benign race: every caller sets the same value
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_kernel<ND, NG>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_limit());
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static DeviceOnce once;
+  hipError_t e = set_dynamic_lds_once(once, reinterpret_cast<const void*>(&split_kernel<ND, NG>),
+                                      lds_limit());
+  if (e != hipSuccess) return e;
   clear_stale_error();
   hipLaunchKernelGGL((split_kernel<ND, NG>), dim3(nblocks), dim3(kThreads), nst * stage, stream,
                      a, stage, nst);

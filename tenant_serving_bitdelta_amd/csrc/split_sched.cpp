@@ -138,16 +138,9 @@ double split_schedule_makespan(const SplitShape& sh, const SplitSched& h) {
 }
 
 int split_compute_units() {
-  static int cached[64];  // per device, 0 = not queried yet (benign race: same value)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 8)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
+  static std::atomic<int> cached[64];  // per device, 0 = not queried yet
+  const int v = device_attribute_cached(cached, hipDeviceAttributeMultiprocessorCount, 256);
+  return v < 8 ? 256 : v;
 }
 
 }  // namespace bd

@@ -295,13 +295,10 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(const StreamArgs a)
 template <int NTW>
 hipError_t launch_ntw(const StreamArgs& a, int nblocks, hipStream_t stream) {
   const size_t lds = stream_lds_bytes(a.ntiles, a.nslots);
-  static bool configured = false;  // benign race: every caller sets the same value
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<NTW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  static DeviceOnce once;
+  hipError_t e = set_dynamic_lds_once(once, reinterpret_cast<const void*>(&stream_kernel<NTW>),
+                                      160 * 1024);
+  if (e != hipSuccess) return e;
   clear_stale_error();
   hipLaunchKernelGGL(stream_kernel<NTW>, dim3(nblocks), dim3(kThreads), lds, stream, a);
   return hipGetLastError();

@@ -89,6 +89,31 @@ def check_alpha_closed_forms(o):
     assert float(o.alpha_ref(np.zeros((3, 32), np.float32))) == 0.0
 
 
+def check_alpha_large_matrices(o):
+    """Matrices above the oracle's exact-summation limit (n = 4096 x 2048 = 2^23 elements, the
+    branch every full-size alpha check of the 70B shapes goes through), against values the
+    mathematics fixes: a constant magnitude with random signs gives that magnitude; a single
+    nonzero c gives |c| / n; the ramp Delta_i = (i - n/4) h over the flattened matrix gives
+    h (m (m + 1) + (n - m - 1)(n - m)) / (2 n) with m = n/4, evaluated here in integers (every
+    partial sum of the ramp is an integer multiple of h below 2^53 h, so an exact fp64 sum is
+    reachable and the expected float32 is the correctly rounded closed form)."""
+    d_out, d_in = 4096, 2048
+    n = d_out * d_in
+    assert n > getattr(o, "FSUM_MAX", 0)
+    rng = np.random.default_rng(3)
+    c = 1.5 * 2.0 ** -12
+    d = (np.where(rng.random((d_out, d_in)) < 0.5, -c, c)).astype(np.float32)
+    assert float(o.alpha_ref(d)) == c
+    d = np.zeros((d_out, d_in), dtype=np.float32)
+    d[1234, 567] = -0.75
+    assert float(o.alpha_ref(d)) == 0.75 / n
+    h, m = 2.0 ** -30, n // 4
+    ramp = ((np.arange(n, dtype=np.int64) - m).astype(np.float64) * h).astype(np.float32)
+    total_over_h = (m * (m + 1) + (n - m - 1) * (n - m)) // 2      # sum of |i - m|, exact integer
+    want = np.float32(total_over_h * 2.0 ** -53)                     # h / n = 2^-53: exact in fp64
+    assert o.alpha_ref(ramp.reshape(d_out, d_in)) == want
+
+
 def check_alpha_least_squares(o):
     """For fixed signs S the best scale minimises ||Delta - a S||_F^2; its minimiser is
     <Delta, S>/n = sum|Delta|/n.  The energy identity ||Delta - alpha S||^2 = ||Delta||^2 - n alpha^2
@@ -309,7 +334,7 @@ def check_alpha_rows_linear(o):
 
 ALL_CHECKS = [
     check_bit_order_golden, check_tiny_linear_golden, check_storage_arithmetic,
-    check_alpha_closed_forms, check_alpha_least_squares, check_laplace_statistics,
+    check_alpha_closed_forms, check_alpha_large_matrices, check_alpha_least_squares, check_laplace_statistics,
     check_signs_and_roundtrip, check_zero_delta_is_plain_product, check_zero_base_isolates_delta,
     check_identity_readback, check_bruteforce_agrees, check_plan_is_stable_sort,
     check_batch_invariance, check_task_vector, check_alpha_rows, check_alpha_rows_linear,
@@ -367,6 +392,20 @@ def _alpha_rms(delta):  # RMS instead of mean absolute value
     return np.float32(np.sqrt(np.mean(np.asarray(delta, dtype=np.float64) ** 2)))
 
 
+def _alpha_large_f32_sum(delta):  # above the exact-summation limit, a float32 accumulation
+    a = np.abs(np.asarray(delta, dtype=np.float64)).ravel()
+    if a.size <= O.FSUM_MAX:
+        return _REAL_ALPHA(delta)
+    return np.float32(float(np.sum(a.astype(np.float32), dtype=np.float32)) / a.size)
+
+
+def _alpha_large_n_minus_one(delta):  # above the limit, the sum divided by n - 1
+    a = np.abs(np.asarray(delta, dtype=np.float64)).ravel()
+    if a.size <= O.FSUM_MAX:
+        return _REAL_ALPHA(delta)
+    return np.float32(float(np.sum(a)) / (a.size - 1))
+
+
 def _reconstruct_minus(w_base, words, alpha):  # wrong sign of the delta term
     wb = np.asarray(w_base, dtype=np.float64)
     return wb - np.float64(np.float32(alpha)) * O.unpack_signs_ref(words, wb.shape[1])
@@ -418,6 +457,7 @@ def _reconstruct_first_row_alpha(w_base, words, alpha):  # alpha[0] used for eve
 
 
 _REAL_RECONSTRUCT = O.reconstruct_ref
+_REAL_ALPHA = O.alpha_ref
 _REAL_MATMUL = O.matmul_ref
 _REAL_PLAN = O.plan_segments_ref
 
@@ -428,6 +468,8 @@ MUTANTS = [
     ("unpack_signs_ref", _unpack_msb_first),
     ("alpha_ref", _alpha_row_mean_of_first_row),
     ("alpha_ref", _alpha_rms),
+    ("alpha_ref", _alpha_large_f32_sum),
+    ("alpha_ref", _alpha_large_n_minus_one),
     ("reconstruct_ref", _reconstruct_minus),
     ("reconstruct_ref", _reconstruct_no_delta),
     ("reconstruct_ref", _reconstruct_transposed_bits),
