@@ -22,11 +22,14 @@
  *     r * (d_in / 32) + k / 32, least-significant bit first; bit 1 means +1, bit 0 means -1.
  *     The byte image of these words equals the BitDelta post's packing of eight sign bits per
  *     int8 ("Infrastructure details", delta storage format).  sign(+0) = sign(-0) = +1.
- *   - Tiled sign words (optional second copy, for the SPLIT decode path; d_in % 128 == 0):
- *     rows are grouped in blocks of 128 and columns in steps of 128; the 4 words of one row and
- *     one step sit at word ((r / 128) * (d_in / 128) + c / 4) * 512 + (r % 128) * 4 + c % 4 for
+ *   - Tiled sign words (the layout the matmul kernels stream; needs d_in % 128 == 0): rows are
+ *     grouped in blocks of 128 and columns in steps of 128; the 4 words of one row and one step
+ *     sit at word ((r / 128) * (d_in / 128) + c / 4) * 512 + (r % 128) * 4 + c % 4 for
  *     row-major word (r, c), so each (block, step) is one contiguous 2 KiB chunk.  The last
  *     block is padded to 128 rows; padding words are never read for output rows < d_out.
+ *     A variant needs its bits resident in ONE layout: the tiled one whenever d_in % 128 == 0
+ *     (every kernel family reads it), the row-major one otherwise.  The row-major form is the
+ *     storage and upload format; bitdelta_upload_variant converts it on the way in.
  *   - bf16 tensors are passed as `const void*` holding IEEE bfloat16 values, row-major.
  *   - d_in must be a multiple of 32 (one word per 32 elements of a row).
  */
@@ -40,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BITDELTA_ABI_VERSION 6
+#define BITDELTA_ABI_VERSION 7
 #define BITDELTA_MAX_VARIANTS 64   /* variant ids 0..63 per matmul call                      */
 #define BITDELTA_MAX_SEGMENTS 65   /* base (-1) plus every variant                            */
 #define BITDELTA_MAX_PROBLEMS 8    /* linears per grouped matmul call                         */
@@ -56,6 +59,7 @@ typedef enum {
 } bitdelta_status;
 
 typedef void* bitdelta_stream; /* hipStream_t */
+typedef void* bitdelta_event;  /* hipEvent_t */
 
 typedef enum { BITDELTA_OUT_BF16 = 0, BITDELTA_OUT_F32 = 1 } bitdelta_out_dtype;
 
@@ -64,7 +68,8 @@ typedef enum { BITDELTA_OUT_BF16 = 0, BITDELTA_OUT_F32 = 1 } bitdelta_out_dtype;
 typedef enum {
   BITDELTA_PATH_AUTO = 0,
   BITDELTA_PATH_GEMV = 1,    /* fp32 reconstruction in registers, VALU; M <= 4                 */
-  BITDELTA_PATH_STREAM = 2,  /* decode: base and sign sums both as bf16 MFMA; no workspace     */
+  BITDELTA_PATH_STREAM = 2,  /* decode: base and sign sums both as bf16 MFMA; no workspace;
+                              * d_in % 128 == 0                                               */
   BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
   BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp6 MFMA on a
                               * two-term fp6 split of alpha * x (per-32-column power-of-two
@@ -72,10 +77,14 @@ typedef enum {
                               * alpha (AUTO runs a batch with a per-row variant on STREAM)    */
 } bitdelta_path;
 
-/* One compressed variant of one weight matrix: the output of bitdelta_compress. */
+/* One compressed variant of one weight matrix: the output of bitdelta_compress.  At least one of
+ * the two word pointers is set; when both are, they hold the same bits and the kernels read the
+ * tiled one.  (ABI 7: either may be NULL.) */
 typedef struct {
-  const uint32_t* sign_words;      /* [dev] d_out * d_in / 32 words, row-major, 4-byte aligned */
-  const uint32_t* sign_words_t128; /* [dev] tiled copy (layout above), 16-byte aligned, or NULL */
+  const uint32_t* sign_words;      /* [dev] d_out * d_in / 32 words, row-major, 4-byte aligned
+                                    * (16-byte aligned for the STREAM path), or NULL           */
+  const uint32_t* sign_words_t128; /* [dev] the tiled layout above, 16-byte aligned (d_in % 128
+                                    * == 0, else SHAPE), or NULL; needed by the SPLIT path     */
   const float* alpha;              /* [dev] the scale: one float32, or d_out (alpha_per_row)   */
   int32_t alpha_per_row;           /* 0: one scale per matrix (bitdelta_compress); 1: one per
                                     * output row, alpha[r] for row r (bitdelta_compress_rows);
@@ -122,19 +131,20 @@ size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in);
  * elements (exact zeros included), and sign(Delta) packed one bit per element.
  *
  *   delta       [dev] float32 [d_out][d_in], 16-byte aligned, finite values.  Read only.
- *   sign_words  [dev] out: uint32 [d_out][d_in/32] (layout above), 4-byte aligned; with
- *               d_in % 128 == 0 and 16-byte alignment the words are written as whole lines
- *               (the faster form), otherwise word by word.
- *   sign_words_t128 [dev] out, optional (NULL = not written): the same bits in the tiled
- *               layout above, bitdelta_sign_words_t128 words, 16-byte aligned; needs
- *               d_in % 128 == 0 (else SHAPE).
+ *   sign_words  [dev] out, optional when sign_words_t128 is given (NULL = not written):
+ *               uint32 [d_out][d_in/32] (layout above), 4-byte aligned; with d_in % 128 == 0
+ *               and 16-byte alignment the words are written as whole lines (the faster form),
+ *               otherwise word by word.
+ *   sign_words_t128 [dev] out, optional when sign_words is given (NULL = not written): the same
+ *               bits in the tiled layout above, bitdelta_sign_words_t128 words, 16-byte
+ *               aligned; needs d_in % 128 == 0 (else SHAPE).
  *   alpha       [dev] out: one float32, the sum of |Delta| (each 4 consecutive elements added
  *               in fp32, those sums in fp64, in a fixed order, so repeated calls are
  *               bit-identical) divided by n and rounded once to float32.
  *   workspace   [dev] at least bitdelta_compress_workspace_bytes(d_out, d_in) bytes,
  *               8-byte aligned; scratch only, contents on return unspecified.
- * Errors: INVALID_ARG (null pointer, d_out <= 0), SHAPE (d_in not a positive multiple of 32),
- * ALIGNMENT, WORKSPACE (workspace_bytes too small), HIP.
+ * Errors: INVALID_ARG (null pointer, both word pointers null, d_out <= 0), SHAPE (d_in not a
+ * positive multiple of 32), ALIGNMENT, WORKSPACE (workspace_bytes too small), HIP.
  * The buffers must not overlap.
  */
 bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
@@ -215,9 +225,15 @@ bitdelta_status bitdelta_plan_segments(const int32_t* token_variant, int64_t M,
  * the path needs none).  AUTO reports what the path AUTO would pick for M needs.  A grouped call
  * needs the sum over its problems.  The SPLIT path keeps there, per token (M rounded up to 16),
  * a bf16 copy of its activations in operand order (2 * d_in bytes), the two fp6 terms of
- * alpha * x (1.5 * d_in bytes) and one scale word per 32 columns (d_in / 8 bytes), and, per
- * linear, 128 fp32 partial-sum slots of 128 rows (512 bytes per token each) plus 128 counters,
- * which the launch uses when it splits a 128-row block's K range over several compute units.
+ * alpha * x (1.5 * d_in bytes), one scale word per 32 columns (d_in / 8 bytes) and one fp32
+ * correction sum per 128 columns (d_in / 32 bytes), each rounded up to 256 bytes, and, per
+ * linear, 128 fp32 partial-sum slots of 128 rows (512 bytes per token each), 128 counters of
+ * 8 bytes, which the launch uses when it splits a 128-row block's K range over several compute
+ * units, and a 256-byte statistics block.  In a call's workspace the slots of all its linears
+ * come first after the activation parts, then all counters, then all statistics blocks; the first
+ * uint32 of the first statistics block counts the split K ranges whose pieces ran on more than
+ * one XCD (the launch intends one XCD per row block; such a handoff is then made coherent with
+ * a device-scope acquire).  The library only ever adds to that word.
  * M = 0 or invalid arguments give 0.
  */
 size_t bitdelta_matmul_workspace_bytes(int64_t M, int64_t d_in, int32_t path);
@@ -257,7 +273,8 @@ bitdelta_status bitdelta_matmul(const void* x, const void* w_base, int64_t M, in
  * one decode batch), enqueued as few launches as possible so small matrices share the GPU.
  * `path` selects the kernel family (bitdelta_path); AUTO picks by M (GEMV for M <= 4, SPLIT
  * for M <= 256, PREFILL above).  SPLIT needs d_in % 128 == 0 and the tiled sign words of every
- * variant the batch uses; STREAM needs d_in % 128 == 0 and 16-byte aligned sign words.  When
+ * variant the batch uses; STREAM needs d_in % 128 == 0 and, for a variant without the tiled
+ * words, 16-byte aligned row-major words.  When
  * AUTO's choice does not apply it falls back SPLIT -> STREAM -> PREFILL; a forced path that does
  * not apply reports UNSUPPORTED.  `workspace` must hold the sum over the problems of
  * bitdelta_matmul_workspace_bytes(M, d_in_p, path), 256-byte aligned.
@@ -276,7 +293,56 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
 int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t* seg_variant,
                            int32_t num_segments);
 
-/* ---- Delta residency (host only, ABI 6) -------------------------------------------------
+/*
+ * bitdelta_reconstruct — the reconstruction of the BitDelta post written out to memory ("Serving
+ * architecture": W_eff = W_base + alpha * sign(Delta), the step the fused kernels keep in
+ * registers).  It exists for the unfused comparison: W_eff materialised in HBM, then a plain
+ * product with it (bitdelta_matmul with the base-model segment, variant -1), against the fused
+ * bitdelta_matmul.
+ *     w_eff[r][k] = bf16_RNE(fp32(w_base[r][k]) + (bit ? +a : -a)),  a = alpha[0] or alpha[r]
+ * with one fp32 addition, as the prefill kernel rebuilds its operands.
+ *
+ *   w_base   [dev] bf16 [d_out][d_in], 16-byte aligned.
+ *   variant  [host] one compressed variant (either word layout; per-matrix or per-row alpha).
+ *   w_eff    [dev] out: bf16 [d_out][d_in], 16-byte aligned, not overlapping the inputs.
+ * Errors: INVALID_ARG (null pointer, d_out <= 0, both word pointers null), SHAPE (d_in not a
+ * positive multiple of 32; tiled words with d_in % 128 != 0), ALIGNMENT, HIP.  ABI 7.
+ */
+bitdelta_status bitdelta_reconstruct(const void* w_base, int64_t d_out, int64_t d_in,
+                                     const bitdelta_variant* variant, void* w_eff,
+                                     bitdelta_stream stream);
+
+/*
+ * bitdelta_upload_variant — move one compressed matrix of a variant from host memory into the
+ * device layout the kernels read (BitDelta post, "Infrastructure details": a variant's delta is
+ * loaded into the GPU's delta cache on its first request; its storage format is the row-major
+ * packing of eight sign bits per byte plus float32 scales).  Enqueued on `stream`: a host-to-
+ * device copy of the row-major words, then (for the tiled layout) one pass that re-lays them
+ * out, and a copy of the scales.  Host buffers in pinned memory (hipHostMalloc) make the copies
+ * asynchronous; pageable ones are copied before the call returns.  Record an event on `stream`
+ * after the call to learn when the variant is usable (see bitdelta_residency_load_enqueued).
+ *
+ *   host_words      [host] uint32 [d_out][d_in/32], row-major (the storage format).
+ *   host_alpha      [host] alpha_count float32 (1, or d_out for per-row scales).
+ *   sign_words      [dev] out, optional: the row-major words (4-byte aligned; 16-byte aligned
+ *                   when the tiled layout is also written, which then reads from it).
+ *   sign_words_t128 [dev] out, optional (d_in % 128 == 0): the tiled layout, 16-byte aligned.
+ *                   At least one of the two is given.
+ *   alpha           [dev] out: alpha_count float32, 4-byte aligned.
+ *   staging         [dev] needed only when sign_words_t128 is given without sign_words: at least
+ *                   d_out * d_in / 8 bytes, 16-byte aligned, scratch; it must not be reused
+ *                   until the work this call enqueues has run (same stream: at once).
+ * Errors: INVALID_ARG (null pointer, sizes <= 0, alpha_count not 1 or d_out, no destination),
+ * SHAPE (d_in % 32, or d_in % 128 for the tiled layout), ALIGNMENT, WORKSPACE (staging missing
+ * or too small), HIP.  ABI 7.
+ */
+bitdelta_status bitdelta_upload_variant(const uint32_t* host_words, const float* host_alpha,
+                                        int64_t alpha_count, int64_t d_out, int64_t d_in,
+                                        uint32_t* sign_words, uint32_t* sign_words_t128,
+                                        float* alpha, void* staging, size_t staging_bytes,
+                                        bitdelta_stream stream);
+
+/* ---- Delta residency (host only, ABI 6; holds and events ABI 7) ---------------------------
  * Which variants' compressed deltas (sign words and alpha) stay in device memory, after the
  * BitDelta post, "Infrastructure details": the variants with the most requests stay pinned (the
  * top few by volume always resident), the rest share the remaining capacity with least-recently-
@@ -284,8 +350,10 @@ int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t*
  * variant whose load is in flight wait for it rather than starting another.  Request rate is the
  * count of requests so far; pinned = the num_pinned highest counts (ties to the smaller id) among
  * variants requested at least once, the current request included.  Pinned and loading variants
- * are never evicted; eviction takes the least recently requested variant first (ties to the
- * smaller id) until the new delta fits.  The caller moves the bytes and calls load_done.
+ * are never evicted; nor are variants held by requests in flight (see `hold` below); eviction
+ * takes the least recently requested evictable variant first (ties to the smaller id) until the
+ * new delta fits.  The caller moves the bytes (bitdelta_upload_variant) and either calls
+ * load_done or attaches the upload's completion event (load_enqueued) for poll to find.
  * Each call locks the manager, so calls from several threads are serialised. */
 typedef struct bitdelta_residency bitdelta_residency;
 
@@ -305,10 +373,33 @@ bitdelta_status bitdelta_residency_create(int32_t num_variants, const int64_t* v
                                           bitdelta_residency** out);
 void bitdelta_residency_destroy(bitdelta_residency* r);
 /* One request for `variant`: *action = BITDELTA_RESIDENCY_*; evicted [host] room for
- * num_variants ids receives the variants dropped, in eviction order, *num_evicted their count.
- * Errors: INVALID_ARG (null pointer, variant out of range). */
-bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t variant, int32_t* action,
-                                           int32_t* evicted, int32_t* num_evicted);
+ * num_variants ids receives the variants dropped, in eviction order, *num_evicted their count
+ * (their memory may be reused once the work that read them has drained).  hold = 1: an answer
+ * HIT, LOAD or QUEUED also makes this request a holder of the variant, which is then never
+ * evicted until every holder has called bitdelta_residency_release (so memory that queued
+ * kernels still read is never handed to another upload, and the variants of one batch, requested
+ * one by one, cannot evict each other); NO_ROOM holds nothing.  hold = 0: no hold.
+ * Errors: INVALID_ARG (null pointer, variant out of range, hold not 0 or 1).  ABI 7 (hold). */
+bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t variant, int32_t hold,
+                                           int32_t* action, int32_t* evicted,
+                                           int32_t* num_evicted);
+/* Drop one hold of `variant` (after the streams that read it have finished the work of the
+ * holding request).  INVALID_ARG if it has no holder.  ABI 7. */
+bitdelta_status bitdelta_residency_release(bitdelta_residency* r, int32_t variant);
+/* Current number of holders of `variant`, or -1 for a bad argument.  ABI 7. */
+int64_t bitdelta_residency_holds(bitdelta_residency* r, int32_t variant);
+/* Attach the event recorded after `variant`'s upload (on the upload's stream) to its load:
+ * bitdelta_residency_poll then makes the variant resident once the event has completed.  The
+ * manager does not own the event; keep it alive until poll has reported the variant (or until
+ * load_done).  INVALID_ARG unless the variant is loading.  ABI 7. */
+bitdelta_status bitdelta_residency_load_enqueued(bitdelta_residency* r, int32_t variant,
+                                                 bitdelta_event event);
+/* Query the events of loading variants; each whose upload has completed becomes resident and is
+ * listed in completed [host, room for num_variants ids] (*num_completed of them): the requests
+ * that were answered QUEUED for it may go ahead.  Never waits.  HIP if an event query fails.
+ * ABI 7. */
+bitdelta_status bitdelta_residency_poll(bitdelta_residency* r, int32_t* completed,
+                                        int32_t* num_completed);
 /* The load of `variant` has finished: it becomes resident.  INVALID_ARG unless it was loading. */
 bitdelta_status bitdelta_residency_load_done(bitdelta_residency* r, int32_t variant);
 /* BITDELTA_VARIANT_* of `variant`, or -1 for a bad argument. */

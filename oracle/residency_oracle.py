@@ -16,11 +16,14 @@ Readings where the post is silent (listed in the design notes):
 * a variant that is loading is neither evictable nor loaded twice; pinned variants are never
   evicted; a request that cannot be made to fit (everything else resident is pinned or loading)
   changes nothing but the counts and is answered "no room";
+* a variant still in use is not "least recently used" in any sense the eviction could mean: a
+  request may hold its variant (answers hit / load / queued), and a held variant is not evicted
+  until every holder has released it;
 * eviction takes the least recently requested evictable variant first (ties to the smaller id),
   one at a time, until the new delta fits in the capacity.
 
-Parity status: pinned by tests/test_residency.py (a hand-derived trace and invariants over random
-traces).
+Parity status: pinned by tests/test_residency.py (hand-derived traces, one of them with holds,
+and invariants over random traces).
 """
 from __future__ import annotations
 
@@ -39,6 +42,7 @@ class ResidencyRef:
         self.count = [0] * n
         self.last = [0] * n   # time of the latest request (0 = never)
         self.state = [ABSENT] * n
+        self.holds = [0] * n  # requests holding the variant, not yet released
         self.clock = 0
 
     def pinned(self):
@@ -48,18 +52,22 @@ class ResidencyRef:
     def used(self) -> int:
         return sum(s for s, st in zip(self.size, self.state) if st != ABSENT)
 
-    def request(self, v: int):
-        """One request for variant v: (action, evicted ids in eviction order)."""
+    def request(self, v: int, hold: bool = False):
+        """One request for variant v: (action, evicted ids in eviction order).  With hold, any
+        answer but "no room" also makes the request a holder of v."""
         self.clock += 1
         self.count[v] += 1
         self.last[v] = self.clock
         if self.state[v] == RESIDENT:
+            self.holds[v] += int(hold)
             return HIT, []
         if self.state[v] == LOADING:
+            self.holds[v] += int(hold)
             return QUEUED, []
         pins = self.pinned()
         evictable = [u for u in range(len(self.size))
-                     if self.state[u] == RESIDENT and u not in pins and u != v]
+                     if self.state[u] == RESIDENT and u not in pins and u != v
+                     and self.holds[u] == 0]
         evictable.sort(key=lambda u: (self.last[u], u))
         need = self.used() + self.size[v] - self.cap
         if need > sum(self.size[u] for u in evictable):
@@ -72,7 +80,13 @@ class ResidencyRef:
             need -= self.size[u]
             evicted.append(u)
         self.state[v] = LOADING
+        self.holds[v] += int(hold)
         return LOAD, evicted
+
+    def release(self, v: int):
+        if self.holds[v] == 0:
+            raise ValueError("variant has no holder")
+        self.holds[v] -= 1
 
     def load_done(self, v: int):
         if self.state[v] != LOADING:

@@ -14,10 +14,12 @@ import numpy as np
 
 __all__ = [
     "BitDeltaError", "lib", "abi_version", "sign_words", "compress_workspace_bytes",
-    "compress_rows", "compress_rows_workspace_bytes",
+    "compress_rows", "compress_rows_workspace_bytes", "compress_from_weights",
     "compress", "plan_segments", "matmul", "matmul_grouped", "auto_path", "PATHS",
-    "matmul_workspace_bytes", "sign_words_t128",
+    "matmul_workspace_bytes", "sign_words_t128", "reconstruct", "upload_variant", "Residency",
 ]
+
+ABI_VERSION = 7
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitdelta.so")
@@ -96,8 +98,26 @@ def _lib():
         L.bitdelta_residency_destroy.restype = None
         L.bitdelta_residency_destroy.argtypes = [ctypes.c_void_p]
         L.bitdelta_residency_request.restype = ctypes.c_int
-        L.bitdelta_residency_request.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p,
-                                                 _i32p]
+        L.bitdelta_residency_request.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                 _i32p, _i32p, _i32p]
+        L.bitdelta_residency_release.restype = ctypes.c_int
+        L.bitdelta_residency_release.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+        L.bitdelta_residency_holds.restype = ctypes.c_int64
+        L.bitdelta_residency_holds.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+        L.bitdelta_residency_load_enqueued.restype = ctypes.c_int
+        L.bitdelta_residency_load_enqueued.argtypes = [ctypes.c_void_p, ctypes.c_int32,
+                                                       ctypes.c_void_p]
+        L.bitdelta_residency_poll.restype = ctypes.c_int
+        L.bitdelta_residency_poll.argtypes = [ctypes.c_void_p, _i32p, _i32p]
+        L.bitdelta_reconstruct.restype = ctypes.c_int
+        L.bitdelta_reconstruct.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.POINTER(_Variant), ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        L.bitdelta_upload_variant.restype = ctypes.c_int
+        L.bitdelta_upload_variant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p]
         L.bitdelta_residency_load_done.restype = ctypes.c_int
         L.bitdelta_residency_load_done.argtypes = [ctypes.c_void_p, ctypes.c_int32]
         L.bitdelta_residency_state.restype = ctypes.c_int32
@@ -149,6 +169,34 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _temp(nbytes, device, stream, dtype_name="uint8"):
+    """A scratch device tensor for one call whose kernels run on ``stream`` (None: torch's
+    current stream).  torch's caching allocator must not hand the block to another tensor while
+    those kernels still use it, so on another stream the block is recorded as in use there."""
+    import torch
+    dtype = getattr(torch, dtype_name)
+    n = max(int(nbytes), 1) // torch.empty((), dtype=dtype).element_size()
+    t = torch.empty(max(n, 1), dtype=dtype, device=device)
+    if stream is not None and int(stream) != torch.cuda.current_stream(device).cuda_stream:
+        t.record_stream(torch.cuda.ExternalStream(int(stream), device=device))
+    return t
+
+
+def _numel_at_least(t, n, what):
+    if t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements, needs at least {n}")
+
+
+def _numel_exact(t, n, what):
+    if t.numel() != n:
+        raise ValueError(f"{what} holds {t.numel()} elements, needs exactly {n}")
+
+
+def _check_shape(t, shape, what):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, needs {tuple(shape)}")
+
+
 _DTYPES = {}
 
 
@@ -183,39 +231,64 @@ def compress_workspace_bytes(d_out: int, d_in: int) -> int:
     return int(_lib().bitdelta_compress_workspace_bytes(d_out, d_in))
 
 
+def _compress_outputs(d_out, d_in, words, tiled, alpha, alpha_n):
+    """Pointers of compress outputs after checking their sizes: ``words`` (int32, d_out * d_in / 32
+    elements) and ``tiled`` (int32, at least sign_words_t128 elements) may each be None, not both."""
+    if words is None and tiled is None:
+        raise ValueError("give the row-major words, the tiled words, or both")
+    if d_in % 32:
+        raise ValueError("d_in must be a multiple of 32")
+    wptr = tptr = None
+    if words is not None:
+        _numel_exact(words, d_out * d_in // 32, "words")
+        wptr = _dev(words, "torch.int32", "words")
+    if tiled is not None:
+        nt = sign_words_t128(d_out, d_in)
+        if nt < 0:
+            raise ValueError("the tiled layout needs d_in % 128 == 0")
+        _numel_at_least(tiled, nt, "tiled sign words")
+        tptr = _dev(tiled, "torch.int32", "tiled sign words")
+    _numel_exact(alpha, alpha_n, "alpha")
+    return wptr, tptr, _dev(alpha, "torch.float32", "alpha")
+
+
+def _workspace_arg(workspace, need, device, stream):
+    """(tensor, pointer, bytes) of a caller's workspace (the library checks its size), or of a
+    scratch tensor sized ``need`` when None."""
+    if workspace is None:
+        workspace = _temp(max(need, 8), device, stream, "float64")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def compress(delta, words, alpha, workspace=None, stream=None, tiled=None):
     """alpha = mean|delta| and packed sign bits of one float32 [d_out, d_in] matrix.
-    ``words``: int32 tensor [d_out, d_in // 32] (uint32 bit patterns), ``alpha``: float32 [1],
-    ``tiled``: optional int32 tensor of sign_words_t128(d_out, d_in) words for the tiled copy."""
-    import torch
+    ``words``: int32 tensor [d_out, d_in // 32] (uint32 bit patterns) or None, ``alpha``: float32
+    [1], ``tiled``: int32 tensor of sign_words_t128(d_out, d_in) words for the tiled layout, or
+    None (at least one of words / tiled)."""
     d_out, d_in = delta.shape
-    if workspace is None:
-        workspace = torch.empty(max(compress_workspace_bytes(d_out, d_in), 8) // 8,
-                                dtype=torch.float64, device=delta.device)
-    tptr = None if tiled is None else _dev(tiled, "torch.int32", "tiled sign words")
+    wptr, tptr, aptr = _compress_outputs(d_out, d_in, words, tiled, alpha, 1)
+    ws, ws_ptr, ws_bytes = _workspace_arg(workspace, compress_workspace_bytes(d_out, d_in),
+                                          delta.device, stream)
     _check(_lib().bitdelta_compress(
-        _dev(delta, "torch.float32", "delta"), d_out, d_in, _dev(words, "torch.int32", "words"),
-        tptr, _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(stream)), "bitdelta_compress")
+        _dev(delta, "torch.float32", "delta"), d_out, d_in, wptr, tptr, aptr, ws_ptr, ws_bytes,
+        _stream(stream)), "bitdelta_compress")
     return words, alpha
 
 
 def compress_from_weights(w_ft, w_base, words, alpha, workspace=None, stream=None, tiled=None):
     """compress() of Delta = w_ft - w_base for two bf16 [d_out, d_in] matrices, Delta never
     formed.  Outputs as for compress()."""
-    import torch
     d_out, d_in = w_base.shape
     if tuple(w_ft.shape) != (d_out, d_in):
         raise ValueError("w_ft and w_base must have the same shape")
-    if workspace is None:
-        workspace = torch.empty(max(compress_workspace_bytes(d_out, d_in), 8) // 8,
-                                dtype=torch.float64, device=w_base.device)
-    tptr = None if tiled is None else _dev(tiled, "torch.int32", "tiled sign words")
+    wptr, tptr, aptr = _compress_outputs(d_out, d_in, words, tiled, alpha, 1)
+    ws, ws_ptr, ws_bytes = _workspace_arg(workspace, compress_workspace_bytes(d_out, d_in),
+                                          w_base.device, stream)
     _check(_lib().bitdelta_compress_from_weights(
         _dev(w_ft, "torch.bfloat16", "w_ft"), _dev(w_base, "torch.bfloat16", "w_base"), d_out, d_in,
-        _dev(words, "torch.int32", "words"), tptr, _dev(alpha, "torch.float32", "alpha"),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)),
-        "bitdelta_compress_from_weights")
+        wptr, tptr, aptr, ws_ptr, ws_bytes, _stream(stream)), "bitdelta_compress_from_weights")
     return words, alpha
 
 
@@ -226,18 +299,13 @@ def compress_rows_workspace_bytes(d_out: int, d_in: int) -> int:
 def compress_rows(delta, words, alpha, workspace=None, stream=None, tiled=None):
     """compress() with one scale per output row: ``alpha`` is float32 [d_out]; pass the result to
     matmul as (words, alpha[, tiled]) and it is applied row by row."""
-    import torch
     d_out, d_in = delta.shape
-    if alpha.numel() != d_out:
-        raise ValueError("alpha must hold one float32 per output row")
-    if workspace is None:
-        workspace = torch.empty(max(compress_rows_workspace_bytes(d_out, d_in), 8) // 8,
-                                dtype=torch.float64, device=delta.device)
-    tptr = None if tiled is None else _dev(tiled, "torch.int32", "tiled sign words")
+    wptr, tptr, aptr = _compress_outputs(d_out, d_in, words, tiled, alpha, d_out)
+    ws, ws_ptr, ws_bytes = _workspace_arg(workspace, compress_rows_workspace_bytes(d_out, d_in),
+                                          delta.device, stream)
     _check(_lib().bitdelta_compress_rows(
-        _dev(delta, "torch.float32", "delta"), d_out, d_in, _dev(words, "torch.int32", "words"),
-        tptr, _dev(alpha, "torch.float32", "alpha"), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(stream)), "bitdelta_compress_rows")
+        _dev(delta, "torch.float32", "delta"), d_out, d_in, wptr, tptr, aptr, ws_ptr, ws_bytes,
+        _stream(stream)), "bitdelta_compress_rows")
     return words, alpha
 
 
@@ -262,13 +330,13 @@ def matmul_workspace_bytes(m: int, d_in: int, path="auto") -> int:
     return int(_lib().bitdelta_matmul_workspace_bytes(m, d_in, PATHS[path]))
 
 
-def _workspace(workspace, need, device):
-    """(pointer, bytes) of the caller's workspace tensor, or of a fresh one when None."""
-    import torch
+def _workspace(workspace, need, device, stream):
+    """(pointer, bytes, tensor) of the caller's workspace tensor, or of a scratch one sized
+    ``need`` when None (none at all when ``need`` is 0)."""
     if workspace is None:
         if need == 0:
             return None, 0, None
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = _temp(need, device, stream)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
@@ -280,22 +348,36 @@ def auto_path(m: int, seg_offsets, seg_variant) -> int:
     return int(_lib().bitdelta_auto_path(m, op, vp, v.size))
 
 
-def _variants_array(variants, d_out):
-    """variants: list of (words, alpha) or (words, alpha, tiled_words) (or None for unused);
+def _variant_struct(v, item, d_out, d_in, i=0):
+    """Fill one _Variant from (words, alpha) or (words, alpha, tiled_words): words (row-major,
+    d_out * d_in / 32 int32) or tiled_words (at least sign_words_t128 int32) may be None, not both;
     alpha holds one float32 (per matrix) or d_out of them (per output row)."""
+    words, alpha = item[0], item[1]
+    tiled = item[2] if len(item) > 2 else None
+    if words is None and tiled is None:
+        raise ValueError(f"variant {i}: needs row-major or tiled sign words")
+    if words is not None:
+        _numel_exact(words, d_out * d_in // 32, f"variant {i} sign words")
+        v.sign_words = _dev(words, "torch.int32", "sign words")
+    if tiled is not None:
+        nt = sign_words_t128(d_out, d_in)
+        if nt < 0:
+            raise ValueError(f"variant {i}: tiled sign words need d_in % 128 == 0")
+        _numel_at_least(tiled, nt, f"variant {i} tiled sign words")
+        v.sign_words_t128 = _dev(tiled, "torch.int32", "tiled sign words")
+    n = alpha.numel()
+    if n != 1 and n != d_out:
+        raise ValueError(f"variant {i}: alpha must hold 1 or d_out = {d_out} values, not {n}")
+    v.alpha = _dev(alpha, "torch.float32", "alpha")
+    v.alpha_per_row = 1 if n > 1 else 0
+
+
+def _variants_array(variants, d_out, d_in):
+    """variants: list of (words, alpha[, tiled_words]) tuples (None for ids the call never uses)."""
     arr = (_Variant * max(len(variants), 1))()
     for i, item in enumerate(variants):
-        if item is None:
-            continue
-        words, alpha = item[0], item[1]
-        arr[i].sign_words = _dev(words, "torch.int32", "sign words")
-        arr[i].alpha = _dev(alpha, "torch.float32", "alpha")
-        n = alpha.numel()
-        if n != 1 and n != d_out:
-            raise ValueError(f"variant {i}: alpha must hold 1 or d_out = {d_out} values, not {n}")
-        arr[i].alpha_per_row = 1 if n > 1 else 0
-        if len(item) > 2 and item[2] is not None:
-            arr[i].sign_words_t128 = _dev(item[2], "torch.int32", "tiled sign words")
+        if item is not None:
+            _variant_struct(arr[i], item, d_out, d_in, i)
     return arr
 
 
@@ -313,20 +395,23 @@ def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="a
     parr = (_Problem * len(problems))()
     keep = []
     for i, (x, w, y, variants) in enumerate(problems):
-        varr = _variants_array(variants, w.shape[0])
+        if w.dim() != 2:
+            raise ValueError("w_base must be [d_out, d_in]")
+        d_out, d_in = int(w.shape[0]), int(w.shape[1])
+        _check_shape(x, (m, d_in), f"problem {i} x")
+        _check_shape(y, (m, d_out), f"problem {i} y")
+        varr = _variants_array(variants, d_out, d_in)
         keep.append(varr)
         parr[i].x = _dev(x, "torch.bfloat16", "x")
         parr[i].w_base = _dev(w, "torch.bfloat16", "w_base")
         parr[i].y = _dev(y, "torch.bfloat16" if out_dtype == "bf16" else "torch.float32", "y")
-        parr[i].d_out, parr[i].d_in = int(w.shape[0]), int(w.shape[1])
+        parr[i].d_out, parr[i].d_in = d_out, d_in
         parr[i].variants = ctypes.cast(varr, ctypes.POINTER(_Variant))
         parr[i].num_variants = len(variants)
-        if x.shape[0] != m or y.shape[0] != m:
-            raise ValueError("x and y must have seg_offsets[-1] rows")
     # the library checks the size of a caller's workspace itself; only a missing one is sized here
     need = 0 if workspace is not None else sum(
         matmul_workspace_bytes(m, int(w.shape[1]), path) for _, w, _, _ in problems)
-    ws_ptr, ws_bytes, ws = _workspace(workspace, need, problems[0][1].device)
+    ws_ptr, ws_bytes, ws = _workspace(workspace, need, problems[0][1].device, stream)
     _check(_lib().bitdelta_matmul_grouped(parr, len(problems), m, offs_p, segv_p, segv.size,
                                           _OUT[out_dtype], PATHS[path], ws_ptr, ws_bytes,
                                           _stream(stream)),
@@ -347,14 +432,18 @@ def matmul(x, w_base, variants, seg_offsets, seg_variant, y=None, out_dtype="bf1
         return y
     offs, offs_p = _i32(seg_offsets)
     segv, segv_p = _i32(seg_variant)
-    varr = _variants_array(variants, w_base.shape[0])
+    if w_base.dim() != 2:
+        raise ValueError("w_base must be [d_out, d_in]")
+    d_out, d_in = int(w_base.shape[0]), int(w_base.shape[1])
+    m = int(offs[-1]) if offs.size else 0
+    _check_shape(x, (m, d_in), "x")
+    _check_shape(y, (m, d_out), "y")
+    varr = _variants_array(variants, d_out, d_in)
     ws_ptr, ws_bytes, ws = _workspace(
-        workspace,
-        0 if workspace is not None else matmul_workspace_bytes(int(x.shape[0]), int(w_base.shape[1])),
-        x.device)
+        workspace, 0 if workspace is not None else matmul_workspace_bytes(m, d_in), x.device, stream)
     _check(_lib().bitdelta_matmul(
         _dev(x, "torch.bfloat16", "x"), _dev(w_base, "torch.bfloat16", "w_base"),
-        int(x.shape[0]), int(w_base.shape[0]), int(w_base.shape[1]), varr, len(variants),
+        m, d_out, d_in, varr, len(variants),
         offs_p, segv_p, segv.size,
         _dev(y, "torch.bfloat16" if out_dtype == "bf16" else "torch.float32", "y"),
         _OUT[out_dtype], ws_ptr, ws_bytes, _stream(stream)), "bitdelta_matmul")
@@ -376,13 +465,38 @@ class Residency:
                                            ctypes.byref(h)), "bitdelta_residency_create")
         self._h = h
 
-    def request(self, v: int):
+    def request(self, v: int, hold: bool = False):
+        """(action, evicted ids).  hold=True: an answer other than NO_ROOM makes this request a
+        holder of v, which is not evicted until release(v)."""
         # output buffers per call, so that threads sharing a manager never read each other's
         ev = (ctypes.c_int32 * self._n)()
         act, ne = ctypes.c_int32(), ctypes.c_int32()
-        _check(_lib().bitdelta_residency_request(self._h, int(v), ctypes.byref(act), ev,
-                                                 ctypes.byref(ne)), "bitdelta_residency_request")
+        _check(_lib().bitdelta_residency_request(self._h, int(v), 1 if hold else 0,
+                                                 ctypes.byref(act), ev, ctypes.byref(ne)),
+               "bitdelta_residency_request")
         return act.value, [ev[i] for i in range(ne.value)]
+
+    def release(self, v: int):
+        _check(_lib().bitdelta_residency_release(self._h, int(v)), "bitdelta_residency_release")
+
+    def holds(self, v: int) -> int:
+        return int(_lib().bitdelta_residency_holds(self._h, int(v)))
+
+    def load_enqueued(self, v: int, event):
+        """Attach the event recorded after v's upload (a torch.cuda.Event that has been
+        recorded); poll() then makes v resident once the event has completed.  Keep the event
+        alive until then."""
+        _check(_lib().bitdelta_residency_load_enqueued(self._h, int(v),
+                                                       ctypes.c_void_p(int(event.cuda_event))),
+               "bitdelta_residency_load_enqueued")
+
+    def poll(self):
+        """Variants whose attached upload event has completed since the last poll (now resident)."""
+        out = (ctypes.c_int32 * self._n)()
+        nc = ctypes.c_int32()
+        _check(_lib().bitdelta_residency_poll(self._h, out, ctypes.byref(nc)),
+               "bitdelta_residency_poll")
+        return [out[i] for i in range(nc.value)]
 
     def load_done(self, v: int):
         _check(_lib().bitdelta_residency_load_done(self._h, int(v)), "bitdelta_residency_load_done")
@@ -398,3 +512,59 @@ class Residency:
         if h is not None and h.value and _LIB is not None:
             _LIB.bitdelta_residency_destroy(h)
             self._h = None
+
+
+def reconstruct(w_base, variant, w_eff=None, stream=None):
+    """W_eff = bf16(W_base + alpha * sign) written to a bf16 [d_out, d_in] tensor (the unfused
+    reconstruction; the fused matmul never forms it).  ``variant``: (words, alpha[, tiled])."""
+    import torch
+    if w_base.dim() != 2:
+        raise ValueError("w_base must be [d_out, d_in]")
+    d_out, d_in = int(w_base.shape[0]), int(w_base.shape[1])
+    if w_eff is None:
+        w_eff = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=w_base.device)
+    _check_shape(w_eff, (d_out, d_in), "w_eff")
+    v = _Variant()
+    _variant_struct(v, variant, d_out, d_in)
+    _check(_lib().bitdelta_reconstruct(_dev(w_base, "torch.bfloat16", "w_base"), d_out, d_in,
+                                       ctypes.byref(v), _dev(w_eff, "torch.bfloat16", "w_eff"),
+                                       _stream(stream)), "bitdelta_reconstruct")
+    return w_eff
+
+
+def upload_variant(host_words, host_alpha, d_out: int, d_in: int, words=None, tiled=None,
+                   alpha=None, staging=None, stream=None):
+    """Host -> device upload of one compressed matrix of a variant, into the layout the kernels
+    read.  ``host_words``: CPU int32 tensor of d_out * d_in / 32 row-major words (pinned memory
+    makes the copy asynchronous); ``host_alpha``: CPU float32 tensor of 1 or d_out scales;
+    ``words`` / ``tiled``: device destinations (at least one); ``alpha``: device float32
+    destination; ``staging``: device scratch of d_out * d_in / 8 bytes when only ``tiled`` is
+    given (allocated here when None).  Returns (words, tiled, alpha)."""
+    import torch
+    if host_words.is_cuda or host_alpha.is_cuda:
+        raise TypeError("host_words and host_alpha must be CPU tensors")
+    if host_words.dtype is not torch.int32 or host_alpha.dtype is not torch.float32:
+        raise TypeError("host_words must be int32 and host_alpha float32")
+    if not host_words.is_contiguous() or not host_alpha.is_contiguous():
+        raise ValueError("host tensors must be contiguous")
+    if d_in % 32:
+        raise ValueError("d_in must be a multiple of 32")
+    _numel_exact(host_words, d_out * d_in // 32, "host_words")
+    na = host_alpha.numel()
+    if na != 1 and na != d_out:
+        raise ValueError("host_alpha must hold 1 or d_out scales")
+    if alpha is None:
+        raise ValueError("a device alpha tensor is required")
+    wptr, tptr, aptr = _compress_outputs(d_out, d_in, words, tiled, alpha, na)
+    sptr, sbytes = None, 0
+    if words is None:
+        nb = d_out * d_in // 8
+        if staging is None:
+            staging = _temp(nb, alpha.device, stream)
+        if not staging.is_cuda or not staging.is_contiguous():
+            raise ValueError("staging must be a contiguous device tensor")
+        sptr, sbytes = staging.data_ptr(), staging.numel() * staging.element_size()
+    _check(_lib().bitdelta_upload_variant(host_words.data_ptr(), host_alpha.data_ptr(), na, d_out,
+                                          d_in, wptr, tptr, aptr, sptr, sbytes, _stream(stream)),
+           "bitdelta_upload_variant")
+    return words, tiled, alpha

@@ -61,12 +61,22 @@ bitdelta_status check_problem(const bitdelta_problem& p, int64_t M,
     if (s.variant >= p.num_variants) return BITDELTA_ERR_INVALID_ARG;
     if (s.variant >= 0) {
       const bitdelta_variant& v = p.variants[s.variant];
-      if (!v.sign_words || !v.alpha) return BITDELTA_ERR_INVALID_ARG;
+      if (!v.alpha || (!v.sign_words && !v.sign_words_t128)) return BITDELTA_ERR_INVALID_ARG;
       if (v.alpha_per_row != 0 && v.alpha_per_row != 1) return BITDELTA_ERR_INVALID_ARG;
-      if (!aligned(v.sign_words, 4) || !aligned(v.alpha, 4)) return BITDELTA_ERR_ALIGNMENT;
+      if (v.sign_words_t128 && p.d_in % 128 != 0) return BITDELTA_ERR_SHAPE;
+      if (!aligned(v.sign_words, 4) || !aligned(v.sign_words_t128, 16) || !aligned(v.alpha, 4))
+        return BITDELTA_ERR_ALIGNMENT;
     }
   }
   return BITDELTA_OK;
+}
+
+// The sign words the kernels read for a variant: the tiled layout when the variant has it (each
+// kernel then streams one 128-row block's words of a step as 2 KiB contiguous), else the
+// row-major words.
+const uint32_t* kernel_words(const bitdelta_variant& v, bool* tiled) {
+  *tiled = v.sign_words_t128 != nullptr;
+  return *tiled ? v.sign_words_t128 : v.sign_words;
 }
 
 int pick_path(int64_t M) {
@@ -81,12 +91,16 @@ size_t workspace_for(int64_t M, int64_t d_in, int path) {
   return path == BITDELTA_PATH_SPLIT ? bd::split_workspace_bytes(M, d_in) : 0;
 }
 
-// The streaming kernels read sign words 16 bytes (4 K steps) per row at a time.
+// The streaming kernels read sign words 16 bytes (4 K steps) per row at a time: the tiled
+// layout, or 16-byte aligned row-major words.
 bool stream_eligible(const bitdelta_problem* probs, int np, const std::vector<Segment>& segs) {
   for (int p = 0; p < np; ++p) {
     if (probs[p].d_in % 128 != 0) return false;
-    for (const Segment& s : segs)
-      if (s.variant >= 0 && !aligned(probs[p].variants[s.variant].sign_words, 16)) return false;
+    for (const Segment& s : segs) {
+      if (s.variant < 0) continue;
+      const bitdelta_variant& v = probs[p].variants[s.variant];
+      if (!v.sign_words_t128 && !aligned(v.sign_words, 16)) return false;
+    }
   }
   return true;
 }
@@ -129,7 +143,9 @@ bitdelta_status run_gemv(const bitdelta_problem* probs, int np, int64_t M,
       int slot = -1;
       if (s.variant >= 0) {
         if (s.variant != last) {
-          a.words[nslot] = P.variants[s.variant].sign_words;
+          bool tiled = false;
+          a.words[nslot] = kernel_words(P.variants[s.variant], &tiled);
+          if (tiled) a.tiled |= 1u << nslot;
           a.alpha[nslot] = P.variants[s.variant].alpha;
           if (P.variants[s.variant].alpha_per_row) a.alpha_rows |= 1u << nslot;
           ++nslot;
@@ -204,8 +220,11 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
         S.d_in = (int)P.d_in;
         S.block_begin = blocks;
         S.alpha_rows = 0;
+        S.tiled = 0;
         for (int s = 0; s < (int)slot_var.size(); ++s) {
-          S.words[s] = P.variants[slot_var[s]].sign_words;
+          bool tiled = false;
+          S.words[s] = kernel_words(P.variants[slot_var[s]], &tiled);
+          if (tiled) S.tiled |= 1u << s;
           S.alpha[s] = P.variants[slot_var[s]].alpha;
           if (P.variants[slot_var[s]].alpha_per_row) S.alpha_rows |= 1u << s;
         }
@@ -347,7 +366,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
                           const std::vector<Segment>& segs, int y_f32, void* workspace,
                           hipStream_t st) {
   // workspace: per problem bf16 pieces, fp6 pieces, block scales; then every problem's share of
-  // partial slots, then of split counters
+  // partial slots, then of split counters, then of statistics blocks
   const int Mp = (int)((M + 15) / 16 * 16);
   std::vector<unsigned char*> xb(np), xq(np), xs(np), xc(np);
   size_t off = 0;
@@ -365,8 +384,11 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
   const int slots_total = np * bd::kSplitSlotsPerLinear;  // counters: as many
   float* partial = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + off);
   // slot_bytes is a multiple of 256, so the slots of all problems end on a 256-byte boundary
-  int32_t* counter = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + off +
-                                                (size_t)slots_total * slot_bytes);
+  unsigned char* after_slots = static_cast<unsigned char*>(workspace) + off +
+                               (size_t)slots_total * slot_bytes;
+  uint64_t* counter = reinterpret_cast<uint64_t*>(after_slots);
+  // statistics: the first word of the first problem's block (it accumulates, never cleared)
+  uint32_t* stats = reinterpret_cast<uint32_t*>(after_slots + (size_t)np * bd::kSplitCounterBytes);
   const int C = bd::split_compute_units() / 8;
   // problems with longer rows first, so the longest workgroups do not form the tail
   std::vector<int> order(np);
@@ -433,6 +455,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
       H.slot_bytes = (uint32_t)slot_bytes;
       H.partial = partial;
       H.counter = counter;
+      H.stats = stats;
       act.counter = counter;
       act.ncounter = 8 * H.nsplit;
       for (int q = 0; q < pn; ++q) {
@@ -512,13 +535,19 @@ bitdelta_status run_prefill(const bitdelta_problem* probs, int np,
       a.y_f32 = y_f32;
       a.n_mtiles = (int)(m1 - m0);
       a.n_ntiles = (int)((P.d_out + bd::kPrefillBN - 1) / bd::kPrefillBN);
-      a.vec_signs = P.d_in % 128 == 0;
+      // bit s of vec_signs: slot s's words are read 16 bytes (one 128-column step) at a time,
+      // which the tiled layout always allows and row-major words when 16-byte aligned
+      const unsigned vec_all = P.d_in % 128 == 0 ? 0xFFFFFFFFu : 0u;
+      a.vec_signs = (int)vec_all;
       a.alpha_rows = 0;
+      a.tiled = 0;
       for (int s = 0; s < (int)slot_var.size(); ++s) {
-        a.words[s] = P.variants[slot_var[s]].sign_words;
+        bool tiled = false;
+        a.words[s] = kernel_words(P.variants[slot_var[s]], &tiled);
+        if (tiled) a.tiled |= 1u << s;
         a.alpha[s] = P.variants[slot_var[s]].alpha;
         if (P.variants[slot_var[s]].alpha_per_row) a.alpha_rows |= 1u << s;
-        if (!aligned(a.words[s], 16)) a.vec_signs = 0;
+        if (!tiled && !aligned(a.words[s], 16)) a.vec_signs &= ~(1 << s);
       }
       bitdelta_status r = map_hip(bd::launch_prefill(a, st));
       if (r != BITDELTA_OK) return r;
@@ -529,6 +558,10 @@ bitdelta_status run_prefill(const bitdelta_problem* probs, int np,
 }
 
 }  // namespace
+
+namespace bd {
+bitdelta_status status_of_hip(hipError_t e) { return map_hip(e); }
+}  // namespace bd
 
 extern "C" {
 
@@ -569,7 +602,8 @@ size_t bitdelta_compress_workspace_bytes(int64_t d_out, int64_t d_in) {
 bitdelta_status bitdelta_compress(const float* delta, int64_t d_out, int64_t d_in,
                                   uint32_t* sign_words, uint32_t* sign_words_t128, float* alpha,
                                   void* workspace, size_t workspace_bytes, bitdelta_stream stream) {
-  if (!delta || !sign_words || !alpha || !workspace) return BITDELTA_ERR_INVALID_ARG;
+  if (!delta || (!sign_words && !sign_words_t128) || !alpha || !workspace)
+    return BITDELTA_ERR_INVALID_ARG;
   if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim)
     return BITDELTA_ERR_INVALID_ARG;
   if (d_in % 32 != 0) return BITDELTA_ERR_SHAPE;
@@ -588,7 +622,8 @@ bitdelta_status bitdelta_compress_from_weights(const void* w_ft, const void* w_b
                                                uint32_t* sign_words_t128, float* alpha,
                                                void* workspace, size_t workspace_bytes,
                                                bitdelta_stream stream) {
-  if (!w_ft || !w_base || !sign_words || !alpha || !workspace) return BITDELTA_ERR_INVALID_ARG;
+  if (!w_ft || !w_base || (!sign_words && !sign_words_t128) || !alpha || !workspace)
+    return BITDELTA_ERR_INVALID_ARG;
   if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim)
     return BITDELTA_ERR_INVALID_ARG;
   if (d_in % 32 != 0) return BITDELTA_ERR_SHAPE;
@@ -604,6 +639,57 @@ bitdelta_status bitdelta_compress_from_weights(const void* w_ft, const void* w_b
                                           static_cast<hipStream_t>(stream)));
 }
 
+bitdelta_status bitdelta_reconstruct(const void* w_base, int64_t d_out, int64_t d_in,
+                                     const bitdelta_variant* variant, void* w_eff,
+                                     bitdelta_stream stream) {
+  if (!w_base || !variant || !w_eff || !variant->alpha ||
+      (!variant->sign_words && !variant->sign_words_t128))
+    return BITDELTA_ERR_INVALID_ARG;
+  if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim) return BITDELTA_ERR_INVALID_ARG;
+  if (variant->alpha_per_row != 0 && variant->alpha_per_row != 1) return BITDELTA_ERR_INVALID_ARG;
+  if (d_in % 32 != 0 || (variant->sign_words_t128 && d_in % 128 != 0)) return BITDELTA_ERR_SHAPE;
+  if (!aligned(w_base, 16) || !aligned(w_eff, 16) || !aligned(variant->sign_words, 4) ||
+      !aligned(variant->sign_words_t128, 16) || !aligned(variant->alpha, 4))
+    return BITDELTA_ERR_ALIGNMENT;
+  bool tiled = false;
+  const uint32_t* words = kernel_words(*variant, &tiled);
+  return map_hip(bd::launch_reconstruct(static_cast<const uint16_t*>(w_base), words, tiled ? 1 : 0,
+                                        variant->alpha, variant->alpha_per_row, d_out, d_in,
+                                        static_cast<uint16_t*>(w_eff),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+bitdelta_status bitdelta_upload_variant(const uint32_t* host_words, const float* host_alpha,
+                                        int64_t alpha_count, int64_t d_out, int64_t d_in,
+                                        uint32_t* sign_words, uint32_t* sign_words_t128,
+                                        float* alpha, void* staging, size_t staging_bytes,
+                                        bitdelta_stream stream) {
+  if (!host_words || !host_alpha || !alpha || (!sign_words && !sign_words_t128))
+    return BITDELTA_ERR_INVALID_ARG;
+  if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim) return BITDELTA_ERR_INVALID_ARG;
+  if (alpha_count != 1 && alpha_count != d_out) return BITDELTA_ERR_INVALID_ARG;
+  if (d_in % 32 != 0 || (sign_words_t128 && d_in % 128 != 0)) return BITDELTA_ERR_SHAPE;
+  const size_t nbytes = (size_t)d_out * (size_t)(d_in / 32) * 4;
+  // the row-major words on the device: the caller's sign_words, else the staging buffer
+  uint32_t* rm = sign_words;
+  if (!rm) {
+    if (!staging || staging_bytes < nbytes) return BITDELTA_ERR_WORKSPACE;
+    rm = static_cast<uint32_t*>(staging);
+  }
+  if (!aligned(alpha, 4) || !aligned(rm, sign_words_t128 ? 16 : 4) || !aligned(sign_words_t128, 16))
+    return BITDELTA_ERR_ALIGNMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bd::clear_stale_error();
+  bitdelta_status r = map_hip(hipMemcpyAsync(rm, host_words, nbytes, hipMemcpyHostToDevice, st));
+  if (r != BITDELTA_OK) return r;
+  if (sign_words_t128) {
+    r = map_hip(bd::launch_retile(rm, d_out, d_in, sign_words_t128, st));
+    if (r != BITDELTA_OK) return r;
+  }
+  return map_hip(hipMemcpyAsync(alpha, host_alpha, (size_t)alpha_count * sizeof(float),
+                                hipMemcpyHostToDevice, st));
+}
+
 size_t bitdelta_compress_rows_workspace_bytes(int64_t d_out, int64_t d_in) {
   if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim || d_in % 32 != 0) return 0;
   return (size_t)bd::compress_rows_partials(d_out, d_in) * sizeof(double);
@@ -613,7 +699,8 @@ bitdelta_status bitdelta_compress_rows(const float* delta, int64_t d_out, int64_
                                        uint32_t* sign_words, uint32_t* sign_words_t128,
                                        float* alpha, void* workspace, size_t workspace_bytes,
                                        bitdelta_stream stream) {
-  if (!delta || !sign_words || !alpha || !workspace) return BITDELTA_ERR_INVALID_ARG;
+  if (!delta || (!sign_words && !sign_words_t128) || !alpha || !workspace)
+    return BITDELTA_ERR_INVALID_ARG;
   if (d_out <= 0 || d_in <= 0 || d_out >= kMaxDim || d_in >= kMaxDim) return BITDELTA_ERR_INVALID_ARG;
   if (d_in % 32 != 0) return BITDELTA_ERR_SHAPE;
   if (sign_words_t128 && d_in % 128 != 0) return BITDELTA_ERR_SHAPE;

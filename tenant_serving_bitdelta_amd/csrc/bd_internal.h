@@ -66,6 +66,18 @@ inline int device_attribute_cached(std::atomic<int>* cache, hipDeviceAttribute_t
 }
 
 // ---------------------------------------------------------------------------------------------
+// Sign-word layouts.  Row-major: word (r, c) at r * wpr + c (wpr = d_in / 32 words per row).
+// 128-row tiled (d_in % 128 == 0): rows in blocks of 128, columns in steps of 128 (4 words), the
+// 4 words of one row and one step at ((r / 128) * (wpr / 4) + c / 4) * 512 + (r % 128) * 4 + c % 4,
+// so one block's words of one step are 2 KiB contiguous.  Either way the 4 words of a row and a
+// 128-column step are 16 contiguous bytes; this is the word offset of word 4q of row r.
+// ---------------------------------------------------------------------------------------------
+__host__ __device__ __forceinline__ size_t sign_quad_offset(bool tiled, int r, int q, int wpr) {
+  return tiled ? ((size_t)(r >> 7) * (size_t)(wpr >> 2) + (size_t)q) * 512 + (size_t)(r & 127) * 4
+               : (size_t)r * (size_t)wpr + 4 * (size_t)q;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Compress (two passes)
 // ---------------------------------------------------------------------------------------------
 // fp64 partials (workspace doubles) pass 1 may write for a d_out x d_in matrix, whichever of
@@ -84,6 +96,15 @@ hipError_t launch_compress_pair(const uint16_t* w_ft, const uint16_t* w_base, in
                                 int64_t d_in, uint32_t* words, uint32_t* tiled, float* alpha,
                                 double* partials, hipStream_t stream);
 
+// W_eff = bf16_RNE(fp32(w) + (+-alpha)) written to HBM (the unfused reconstruction); words in
+// either layout (tiled != 0: the 128-row tiled layout, d_in % 128 == 0).
+hipError_t launch_reconstruct(const uint16_t* w, const uint32_t* words, int tiled,
+                              const float* alpha, int alpha_per_row, int64_t d_out, int64_t d_in,
+                              uint16_t* w_eff, hipStream_t stream);
+// row-major sign words [d_out][d_in/32] (device) -> the 128-row tiled layout (d_in % 128 == 0)
+hipError_t launch_retile(const uint32_t* src, int64_t d_out, int64_t d_in, uint32_t* dst,
+                         hipStream_t stream);
+
 // ---------------------------------------------------------------------------------------------
 // Matmul kernels
 // ---------------------------------------------------------------------------------------------
@@ -101,6 +122,7 @@ struct GemvArgs {
   const uint32_t* words[4];
   const float* alpha[4];
   unsigned alpha_rows;  // bit s set: slot s has one alpha per output row
+  unsigned tiled;       // bit s set: slot s's words are in the 128-row tiled layout
 };
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
@@ -117,6 +139,8 @@ struct StreamProblem {
   int d_out, d_in;
   int block_begin;
   unsigned alpha_rows;  // bit s set: slot s has one alpha per output row
+  unsigned tiled;       // bit s set: slot s's words are in the 128-row tiled layout
+  unsigned pad_;
   const uint32_t* words[kMaxSlots];
   const float* alpha[kMaxSlots];
 };
@@ -141,8 +165,12 @@ struct PrefillArgs {
   const uint16_t* w;
   void* y;
   int d_out, d_in, y_f32, n_mtiles, n_ntiles;
-  int vec_signs;                       // every words[] 16-byte aligned and d_in % 128 == 0
+  int vec_signs;                       // bit s set: slot s's words are read 16 bytes (4 steps)
+                                       // at a time (d_in % 128 == 0 and tiled or 16-byte aligned
+                                       // row-major words); bit 31: base-model tiles
   unsigned alpha_rows;                 // bit s set: slot s has one alpha per output row
+  unsigned tiled;                      // bit s set: slot s's words are in the 128-row tiled
+                                       // layout (then its vec_signs bit is set)
   const uint32_t* words[kMaxSlots];
   const float* alpha[kMaxSlots];
   // per M-tile: first x row, rows in the tile (1..256), variant slot (-1 = base)
@@ -192,7 +220,8 @@ struct SplitWave {
 // same steps of different units come one after another, so they run side by side and share
 // the activations in L2.  A unit done in several pieces is "split": each piece leaves its fp32
 // sums in a partial slot, and the piece that finishes last adds the slots in piece order and
-// writes y.
+// writes y.  A split unit's counter (64 bits) holds in bits 0..7 the pieces counted in and in
+// bits 8 + 6x .. 13 + 6x the pieces that ran on XCD x.
 struct SplitSched {
   int32_t head[kMaxProblems];            // steps of the first piece of every unit of linear q
   int32_t pooled[kMaxProblems];          // trailing units of linear q done in the pool
@@ -201,7 +230,8 @@ struct SplitSched {
   int32_t nsplit, nslot;                 // split units and partial slots per XCD
   uint32_t slot_bytes;                   // bytes of one partial slot (128 rows x 4 x Mp)
   float* partial;                        // [8][nslot] partial slots
-  int32_t* counter;                      // [8][nsplit] finished pieces per split unit
+  uint64_t* counter;                     // [8][nsplit] finished pieces per split unit
+  uint32_t* stats;                       // [0]: handoffs whose pieces ran on several XCDs
 };
 
 // Piece kk of an XCD's list under schedule H, for linears with ns[q] K steps and nb[q] row
@@ -295,19 +325,21 @@ struct SplitActArgs {
   const float* alpha[kMaxProblems][kMaxSlots];
   int d_in[kMaxProblems];
   int Mp, tok_base, lo, hi, nprob, pad_;  // tokens [tok_base + lo, tok_base + hi)
-  int32_t* counter;                    // out: ncounter split counters set to zero
+  uint64_t* counter;                   // out: ncounter split counters set to zero
   int ncounter, pad2_;
   int8_t token_slot[kSplitMaxM];       // slot of token tok_base + t (-1 = base model); read per lane
 };
 hipError_t launch_split_act(const SplitActArgs& a, hipStream_t stream);
 // Workspace of one linear: bf16 pieces, fp6 pieces, scales, correction sums, and its share of
-// the call's partial slots and split counters (kSplitSlotsPerLinear of each); each part a
-// multiple of 256 bytes.
+// the call's partial slots and split counters (kSplitSlotsPerLinear of each) and a 256-byte
+// statistics block; each part a multiple of 256 bytes.
 constexpr int kSplitSlotsPerLinear = 128;
 size_t split_workspace_bytes(int64_t M, int64_t d_in);
 void split_workspace_parts(int64_t M, int64_t d_in, size_t* xb_bytes, size_t* xq_bytes,
                            size_t* xs_bytes, size_t* xc_bytes);
-size_t split_partial_bytes(int64_t M);   // one linear's share of partial slots and counters
+size_t split_partial_bytes(int64_t M);   // one linear's share of partial slots, counters, stats
+constexpr size_t kSplitCounterBytes = (size_t)kSplitSlotsPerLinear * 8;  // per linear
+constexpr size_t kSplitStatsBytes = 256;                                 // per linear
 size_t split_slot_bytes(int64_t M);      // one partial slot
 
 }  // namespace bd

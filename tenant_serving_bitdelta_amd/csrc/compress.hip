@@ -20,8 +20,9 @@
 // Pass 2 sums the partials in a fixed order and rounds sum/n once to float32, so the result is
 // identical from run to run (no atomics anywhere).
 //
-// Optionally pass 1 also writes a second copy of the sign words in the tiled layout the
-// split-activation decode kernel streams: for every block of 128 rows and every 128-column step,
+// Pass 1 writes the row-major words, the tiled layout below, or both (either pointer may be
+// null, not both).  The tiled layout is the one every matmul kernel streams: for every block of
+// 128 rows and every 128-column step,
 // the 4 words of each of the 128 rows lie in one contiguous 2 KiB chunk,
 //   tiled word ((r / 128) * (d_in / 128) + c / 4) * 512 + (r % 128) * 4 + c % 4  <-  word (r, c),
 // so a block's sign words for one step are read as whole cache lines.  Rows past d_out in the
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void compress_pass1(const f32x4* __restri
       // n is a multiple of 32, so the 8 lanes of a word are all in range or all out of range.
       if ((lane & 7) == 0 && ok[u]) {
         const int64_t w = i >> 3;
-        words[w] = part;
+        if (words) words[w] = part;
         if (tiled) {
           if (kSmall) {
             const unsigned w32 = (unsigned)w, wpr32 = (unsigned)wpr;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_tiles(
       if (lane == 0 && r < d_out) partials[r * ncg + cg] = tacc;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0 && words) {
       // plain words: lane = (row, 4-word group); the 8 lanes of a row fill its 128-byte line
       const int row = lane >> 3, q = lane & 7;
       const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void compress_pair_tiles(
       if ((lane & 3) == 0) tw[buf][wave][u * 16 + (lane >> 2)] = part;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0 && words) {
       const int row = lane >> 3, q = lane & 7;
       const int64_t rr = rg * kTileWaves + row, wc = cg * (kTileCols / 32) + q * 4;
       if (rr < d_out && wc < wpr) {

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
       for (int t = 0; t < M; ++t) {
         if (slot[t] >= 0 && fresh[t])
-          word[t] = a.words[slot[t]][(size_t)rowc[r] * wpr + wi];
+          word[t] = a.words[slot[t]][sign_quad_offset((a.tiled >> slot[t]) & 1u, rowc[r], wi >> 2,
+                                                      wpr) + (wi & 3)];
         else
           word[t] = t > 0 ? word[t - 1] : 0u;
       }

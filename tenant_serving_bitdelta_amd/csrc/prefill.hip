@@ -152,18 +152,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   };
 
   // ---- sign words: lane (j, g) of row tile rt holds the 4 words of row 32w + 16rt + j for a quad
-  const rsrc_t srs = make_rsrc(slot >= 0 ? static_cast<const void*>(a.words[slot] + (size_t)n0 * wpr)
-                                         : static_cast<const void*>(a.w));
+  // row-major words: the tile's rows start at word n0 * wpr; tiled words (n0 is a multiple of
+  // 256, so the tile starts a 128-row block): at word (n0 / 128) * (wpr / 4) * 512
+  const bool tiled = slot >= 0 && ((a.tiled >> slot) & 1u);
+  const rsrc_t srs = make_rsrc(
+      slot >= 0 ? static_cast<const void*>(a.words[slot] + sign_quad_offset(tiled, n0, 0, wpr))
+                : static_cast<const void*>(a.w));
   unsigned soff[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
-    soff[rt] = (unsigned)((min(n0 + 32 * wave + 16 * rt + j, d_out - 1) - n0) * wpr) * 4u;
-  const bool vec_signs = a.vec_signs != 0;
+    soff[rt] = (unsigned)sign_quad_offset(tiled, min(n0 + 32 * wave + 16 * rt + j, d_out - 1) - n0,
+                                          0, wpr) * 4u;
+  // 16-byte quads of words: the slot's bit of vec_signs; base-model tiles read (and ignore) W_base
+  // bytes, 16 at a time whenever d_in % 128 == 0
+  const bool vec_signs = ((unsigned)a.vec_signs >> (slot >= 0 ? slot : 31)) & 1u;
+  const unsigned quad_bytes = tiled ? 2048u : 16u;  // bytes between the words of two quads
   auto load_s = [&](u32x4* sw, int q0, int rt) {  // the quad starting at step q0 (clamped)
     if (vec_signs) {
       const int qc = min(q0, (nsteps - 1) & ~3);
       sw[rt] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, soff[rt] + (unsigned)qc * 4u, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, soff[rt] + (unsigned)(qc >> 2) * quad_bytes,
+                                                        0, 0));
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t)

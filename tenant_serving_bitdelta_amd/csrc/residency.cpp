@@ -1,17 +1,22 @@
-// Delta residency manager (host only): decides which variants' compressed deltas stay in device
-// memory.  It follows the BitDelta post, "Infrastructure details": the variants with the most
-// requests stay pinned (the top few by volume are always resident), the others share the rest of
-// the space with least-recently-used eviction; a request for a variant that is not resident
-// starts a load (cold start); requests for a variant whose load is in flight wait for it instead
-// of starting another (request routing).
+// Delta residency manager: decides which variants' compressed deltas stay in device memory, and
+// ties a load's completion to the HIP event the upload recorded.  It follows the BitDelta post,
+// "Infrastructure details": the variants with the most requests stay pinned (the top few by
+// volume are always resident), the others share the rest of the space with least-recently-used
+// eviction; a request for a variant that is not resident starts a load (cold start); requests for
+// a variant whose load is in flight wait for it instead of starting another (request routing).
 //
 // Request rate is the number of requests seen so far; the pinned set is the num_pinned variants
 // with the highest counts (ties to the smaller id) among those requested at least once, counting
 // the current request.  Loading variants are neither evicted nor loaded twice; pinned variants
-// are never evicted; eviction takes the least recently requested evictable variant first (ties to
-// the smaller id) until the new delta fits; a request that cannot be made to fit changes nothing
-// but the request counts and is answered NO_ROOM.  The caller moves the bytes (an upload on its
-// own stream) and reports the end of each load.
+// and variants held by requests in flight are never evicted; eviction takes the least recently
+// requested evictable variant first (ties to the smaller id) until the new delta fits; a request
+// that cannot be made to fit changes nothing but the request counts and is answered NO_ROOM.
+// A request may hold its variant (the answer HIT, LOAD or QUEUED then counts one more holder);
+// the caller releases it when the work that reads the variant's memory has drained.  The caller
+// moves the bytes (bitdelta_upload_variant on its stream, say); it reports the end of a load
+// with load_done, or attaches the event recorded after the upload and lets poll find it done.
+#include <hip/hip_runtime.h>
+
 #include <algorithm>
 #include <mutex>
 #include <numeric>
@@ -19,11 +24,17 @@
 
 #include "../../include/bitdelta.h"
 
+namespace bd {
+bitdelta_status status_of_hip(hipError_t e);  // records e for bitdelta_last_hip_error
+}
+
 struct bitdelta_residency {
   std::vector<int64_t> size;
   std::vector<int64_t> count;
-  std::vector<uint64_t> last;  // time of the latest request, 0 = never
-  std::vector<uint8_t> state;  // BITDELTA_VARIANT_*
+  std::vector<uint64_t> last;    // time of the latest request, 0 = never
+  std::vector<uint8_t> state;    // BITDELTA_VARIANT_*
+  std::vector<int64_t> holds;    // requests holding the variant (not yet released)
+  std::vector<hipEvent_t> done;  // event of a loading variant's upload, or null
   int64_t cap = 0;
   int64_t used = 0;
   int32_t num_pinned = 0;
@@ -69,6 +80,8 @@ bitdelta_status bitdelta_residency_create(int32_t num_variants, const int64_t* v
   r->count.assign(num_variants, 0);
   r->last.assign(num_variants, 0);
   r->state.assign(num_variants, BITDELTA_VARIANT_ABSENT);
+  r->holds.assign(num_variants, 0);
+  r->done.assign(num_variants, nullptr);
   r->cap = capacity_bytes;
   r->num_pinned = num_pinned;
   *out = r;
@@ -77,9 +90,11 @@ bitdelta_status bitdelta_residency_create(int32_t num_variants, const int64_t* v
 
 void bitdelta_residency_destroy(bitdelta_residency* r) { delete r; }
 
-bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t variant, int32_t* action,
-                                           int32_t* evicted, int32_t* num_evicted) {
-  if (!r || !action || !evicted || !num_evicted) return BITDELTA_ERR_INVALID_ARG;
+bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t variant, int32_t hold,
+                                           int32_t* action, int32_t* evicted,
+                                           int32_t* num_evicted) {
+  if (!r || !action || !evicted || !num_evicted || (hold != 0 && hold != 1))
+    return BITDELTA_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> lock(r->mu);
   const int n = (int)r->size.size();
   if (variant < 0 || variant >= n) return BITDELTA_ERR_INVALID_ARG;
@@ -88,17 +103,19 @@ bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t varian
   r->last[variant] = ++r->clock;
   if (r->state[variant] == BITDELTA_VARIANT_RESIDENT) {
     *action = BITDELTA_RESIDENCY_HIT;
+    r->holds[variant] += hold;
     return BITDELTA_OK;
   }
   if (r->state[variant] == BITDELTA_VARIANT_LOADING) {
     *action = BITDELTA_RESIDENCY_QUEUED;
+    r->holds[variant] += hold;
     return BITDELTA_OK;
   }
   const std::vector<uint8_t> pin = pinned_set(*r);
   std::vector<int32_t> cand;
   int64_t freeable = 0;
   for (int u = 0; u < n; ++u)
-    if (u != variant && r->state[u] == BITDELTA_VARIANT_RESIDENT && !pin[u]) {
+    if (u != variant && r->state[u] == BITDELTA_VARIANT_RESIDENT && !pin[u] && r->holds[u] == 0) {
       cand.push_back(u);
       freeable += r->size[u];
     }
@@ -119,10 +136,28 @@ bitdelta_status bitdelta_residency_request(bitdelta_residency* r, int32_t varian
     evicted[ne++] = u;
   }
   r->state[variant] = BITDELTA_VARIANT_LOADING;
+  r->done[variant] = nullptr;
   r->used += r->size[variant];
+  r->holds[variant] += hold;
   *num_evicted = ne;
   *action = BITDELTA_RESIDENCY_LOAD;
   return BITDELTA_OK;
+}
+
+bitdelta_status bitdelta_residency_release(bitdelta_residency* r, int32_t variant) {
+  if (!r) return BITDELTA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(r->mu);
+  if (variant < 0 || variant >= (int)r->size.size() || r->holds[variant] == 0)
+    return BITDELTA_ERR_INVALID_ARG;
+  r->holds[variant] -= 1;
+  return BITDELTA_OK;
+}
+
+int64_t bitdelta_residency_holds(bitdelta_residency* r, int32_t variant) {
+  if (!r) return -1;
+  std::lock_guard<std::mutex> lock(r->mu);
+  if (variant < 0 || variant >= (int)r->size.size()) return -1;
+  return r->holds[variant];
 }
 
 bitdelta_status bitdelta_residency_load_done(bitdelta_residency* r, int32_t variant) {
@@ -132,6 +167,39 @@ bitdelta_status bitdelta_residency_load_done(bitdelta_residency* r, int32_t vari
       r->state[variant] != BITDELTA_VARIANT_LOADING)
     return BITDELTA_ERR_INVALID_ARG;
   r->state[variant] = BITDELTA_VARIANT_RESIDENT;
+  r->done[variant] = nullptr;
+  return BITDELTA_OK;
+}
+
+bitdelta_status bitdelta_residency_load_enqueued(bitdelta_residency* r, int32_t variant,
+                                                 bitdelta_event event) {
+  if (!r || !event) return BITDELTA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(r->mu);
+  if (variant < 0 || variant >= (int)r->size.size() ||
+      r->state[variant] != BITDELTA_VARIANT_LOADING)
+    return BITDELTA_ERR_INVALID_ARG;
+  r->done[variant] = static_cast<hipEvent_t>(event);
+  return BITDELTA_OK;
+}
+
+bitdelta_status bitdelta_residency_poll(bitdelta_residency* r, int32_t* completed,
+                                        int32_t* num_completed) {
+  if (!r || !completed || !num_completed) return BITDELTA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(r->mu);
+  int32_t nc = 0;
+  for (int v = 0; v < (int)r->size.size(); ++v) {
+    if (r->state[v] != BITDELTA_VARIANT_LOADING || !r->done[v]) continue;
+    const hipError_t e = hipEventQuery(r->done[v]);
+    if (e == hipErrorNotReady) continue;
+    if (e != hipSuccess) {
+      *num_completed = nc;
+      return bd::status_of_hip(e);
+    }
+    r->state[v] = BITDELTA_VARIANT_RESIDENT;
+    r->done[v] = nullptr;
+    completed[nc++] = v;
+  }
+  *num_completed = nc;
   return BITDELTA_OK;
 }
 

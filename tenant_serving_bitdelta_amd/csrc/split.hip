@@ -401,12 +401,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 
   // ---- split unit: leave the sums in this piece's slot; the last piece adds all slots ------------
   // A slot holds, per dense tile i of the launch and row tile rt, the 64 lanes' f32x4 in lane
-  // order, so each wave reads back exactly what the same wave of another piece wrote.  Every
-  // piece of a unit runs on the same XCD, whose L2 all its compute units share: the slots are
-  // written and read with device-coherent accesses (which skip the compute unit's own cache),
-  // each wave waits until its stores are done before the workgroup counts itself in, and the
-  // workgroup that brings the count to nparts adds the slots in piece order (its own sums from
-  // registers, so the order, and the result, do not depend on which piece finished last).
+  // order, so each wave reads back exactly what the same wave of another piece wrote.  The slots
+  // are written and read with device-coherent accesses (which skip the compute unit's own
+  // cache); each wave waits until its stores are done, then one thread releases them at device
+  // scope (the XCD's L2 writes back what it holds) and counts the piece in, adding 1 to the
+  // count and 1 to the field of the XCD it runs on.  The workgroup that brings the count to
+  // nparts adds the slots in piece order (its own sums from registers, so the order, and the
+  // result, do not depend on which piece finished last).  The schedule puts every piece of a
+  // unit on one XCD (workgroups b and b + 8k are dispatched to the same XCD), so the slots meet
+  // in that XCD's L2; if the fields show pieces on another XCD, the last piece first acquires at
+  // device scope (invalidating stale lines of its L2) and counts the event in the stats word.
   if (nparts > 1) {
     const rsrc_t prs = make_rsrc(reinterpret_cast<unsigned char*>(H.partial) +
                                  (size_t)(xcd * H.nslot + slot0) * H.slot_bytes);
@@ -423,11 +427,24 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     SPLIT_VMCNT(0);
     __syncthreads();
     int* flag = reinterpret_cast<int*>(smem);
-    if (tid == 0)
-      flag[0] = __hip_atomic_fetch_add(H.counter + xcd * H.nsplit + sid, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      unsigned hw;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw));
+      const unsigned x = hw & 7u;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const unsigned long long old = __hip_atomic_fetch_add(
+          H.counter + xcd * H.nsplit + sid, 1ull + (1ull << (8 + 6 * x)), __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = (int)(old & 0xFFu) == nparts - 1;
+      const bool elsewhere = ((old >> 8) & ~(0x3Full << (6 * x))) != 0ull;
+      if (last && elsewhere) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_fetch_add(H.stats, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      flag[0] = last ? 1 : 0;
+    }
     __syncthreads();
-    if (flag[0] != nparts - 1) return;  // workgroup-uniform: another piece finishes this unit
+    if (flag[0] == 0) return;  // workgroup-uniform: another piece finishes this unit
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       if (!dreal[i]) continue;
@@ -669,7 +686,7 @@ size_t split_slot_bytes(int64_t M) {
 
 size_t split_partial_bytes(int64_t M) {
   return round256((size_t)kSplitSlotsPerLinear * split_slot_bytes(M)) +
-         round256((size_t)kSplitSlotsPerLinear * 4);
+         round256(kSplitCounterBytes) + kSplitStatsBytes;
 }
 
 size_t split_workspace_bytes(int64_t M, int64_t d_in) {
@@ -724,7 +741,7 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
   // the schedule must describe the lists the kernel walks (see the piece map in the kernel)
   const SplitSched& H = a.sch;
   if (H.sigma < 1) return hipErrorInvalidValue;
-  int nheads = 0, npool = 0, nsplit = 0, nslot = 0;
+  int nheads = 0, npool = 0, nsplit = 0, nslot = 0, max_parts = 1;
   for (int q = 0; q < a.nprob; ++q) {
     const SplitProblem& P = a.prob[q];
     if (P.nblocks < 1 || P.d_in < kKS || P.d_in % kKS != 0) return hipErrorInvalidValue;
@@ -739,10 +756,14 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
     npool += ncut * tp + H.pooled[q] * pp;
     nsplit += ncut + H.pooled[q];
     nslot += ncut * (1 + tp) + H.pooled[q] * pp;
+    if (ncut > 0) max_parts = max(max_parts, 1 + tp);
+    if (H.pooled[q] > 0) max_parts = max(max_parts, pp);
   }
+  // a unit's counter has 6 bits per XCD field and 8 for the count
+  if (max_parts > 63) return hipErrorInvalidValue;
   if (nheads != H.nheads || npool != H.npool || nsplit != H.nsplit || nslot != H.nslot)
     return hipErrorInvalidValue;
-  if (nslot > 0 && (!H.partial || !H.counter || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
+  if (nslot > 0 && (!H.partial || !H.counter || !H.stats || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
     return hipErrorInvalidValue;
   const int nblocks = 8 * (nheads + npool);
   if (nd == 1) {

@@ -38,8 +38,13 @@ bool same_shape(const SplitShape& a, const SplitShape& b) {
   return true;
 }
 
-// list lengths, split units and partial slots of one XCD's list (the kernel's piece map)
-void count_pieces(const SplitShape& sh, SplitSched* h) {
+// Pieces of one unit the kernel's counter can count: 6 bits per XCD field.
+constexpr int kMaxParts = 63;
+
+// list lengths, split units and partial slots of one XCD's list (the kernel's piece map); the
+// return value is the largest number of pieces of one unit
+int count_pieces(const SplitShape& sh, SplitSched* h) {
+  int max_parts = 1;
   h->nheads = h->npool = h->nsplit = h->nslot = 0;
   for (int q = 0; q < sh.np; ++q) {
     const int cnt = (sh.nb[q] + 7) >> 3;
@@ -51,7 +56,10 @@ void count_pieces(const SplitShape& sh, SplitSched* h) {
     h->npool += ncut * tp + h->pooled[q] * pp;
     h->nsplit += ncut + h->pooled[q];
     h->nslot += ncut * (1 + tp) + h->pooled[q] * pp;
+    if (ncut > 0) max_parts = std::max(max_parts, 1 + tp);
+    if (h->pooled[q] > 0) max_parts = std::max(max_parts, pp);
   }
+  return max_parts;
 }
 
 // Makespan, in K steps, of one XCD's list (with the largest eighth of every linear) on sh.C
@@ -100,8 +108,7 @@ SplitSched choose(const SplitShape& sh) {
           c.pooled[q] = q == last ? pooled : 0;
         }
         c.sigma = sigma;
-        count_pieces(sh, &c);
-        if (c.nslot > sh.slots_avail) continue;
+        if (count_pieces(sh, &c) > kMaxParts || c.nslot > sh.slots_avail) continue;
         const double t = simulate(sh, c, c_piece, c_part);
         if (t < best_t - 1e-9 || (t < best_t + 1e-9 && c.nslot < best.nslot)) {
           best = c;

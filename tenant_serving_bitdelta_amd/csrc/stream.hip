@@ -164,8 +164,9 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(const StreamArgs a)
   auto load_bits = [&](int ks, int set) {
     const int grp = min((ks >> 2) + 1, (nsteps - 1) >> 2);
     const int widx = min(grp * 8 + bhalf * 4, wpr - 4);
+    const int sl = bits_slot(ks);
     br[set] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        a.prob[p].words[bits_slot(ks)] + (size_t)bgrow * wpr + widx));
+        a.prob[p].words[sl] + sign_quad_offset((a.prob[p].tiled >> sl) & 1u, bgrow, widx >> 2, wpr)));
   };
   auto store_bits = [&](int ks, int set) {
     const int grp = (ks >> 2) + 1;
@@ -187,7 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(const StreamArgs a)
   for (int quarter = 0; quarter < 4; ++quarter) {  // sign-word group 0 straight into BS[0]
     const int slot = bits_slot(quarter);
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        a.prob[p].words[slot] + (size_t)bgrow * wpr + min(bhalf * 4, wpr - 4)));
+        a.prob[p].words[slot] + sign_quad_offset((a.prob[p].tiled >> slot) & 1u, bgrow,
+                                                 min(bhalf * 4, wpr - 4) >> 2, wpr)));
     *lds_at<u32x4>(BS, slot * kRows * kBitsRowBytes + bdst) = v;
   }
   load_x(0, 0);

@@ -37,7 +37,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.abi_version() == 6
+    assert bd.abi_version() == bd.ABI_VERSION == 7
     for s in range(7):
         assert L.bitdelta_status_string(s)
     assert L.bitdelta_status_string(99) == b"unknown status"
@@ -210,6 +210,10 @@ def test_matmul_validation():
     assert call(y=FAKE + 4) == ALIGN
     assert call(variants=[(FAKE + 2, FAKE), (FAKE, FAKE)]) == ALIGN
     assert call(variants=[(None, FAKE), (FAKE, FAKE)]) == INVALID
+    # tiled words alone are a complete variant, but need d_in % 128 == 0 and 16-byte alignment
+    assert call(variants=[(None, FAKE, FAKE), (FAKE, FAKE)]) == SHAPE
+    assert call(d_in=128, variants=[(None, FAKE, FAKE + 4), (FAKE, FAKE)], path=3) == ALIGN
+    assert call(variants=[(None, None, FAKE), (FAKE, FAKE)]) == INVALID
     assert call(y_dtype=7) == INVALID
     assert call(path=9) == INVALID
     assert call(path=1) == UNSUPPORTED            # the GEMV path takes at most 4 tokens
@@ -247,9 +251,10 @@ def test_matmul_workspace_bytes():
     # per token (M rounded up to 16): a bf16 copy (2 bytes per element), the two fp6 terms
     # (1.5 bytes per element) and one 4-byte scale word per 32 elements, each region rounded
     # up to 256 bytes; then the linear's share of the call's partial slots (128 slots of
-    # 128 rows x 4 bytes per token) and of its split counters (128 x 4 bytes)
+    # 128 rows x 4 bytes per token), of its split counters (128 x 8 bytes) and a 256-byte
+    # statistics block
     # and one fp32 correction sum per token and 128 columns
-    part = lambda mp: 128 * 128 * 4 * mp + 512
+    part = lambda mp: 128 * 128 * 4 * mp + 128 * 8 + 256
     assert bd.matmul_workspace_bytes(256, 8192) == (256 * 8192 * 2 + 256 * 8192 * 3 // 2
                                                     + 256 * 8192 // 8 + 256 * 8192 // 32 + part(256))
     assert bd.matmul_workspace_bytes(5, 128, "split") == (16 * 128 * 2 + 16 * 128 * 3 // 2 + 256
@@ -268,3 +273,58 @@ def test_auto_path_choice():
     assert bd.auto_path(256, [0, 100, 256], [-1, 5]) == 4
     assert bd.auto_path(8192, [0, 2048, 4096, 6144, 8192], [0, 1, 2, 3]) == 3
     assert bd.auto_path(8, [0, 9], [0]) == -1
+
+
+def _variant(words=FAKE, alpha=FAKE, tiled=None, per_row=0):
+    v = bd._Variant()
+    v.sign_words, v.alpha, v.sign_words_t128, v.alpha_per_row = words, alpha, tiled, per_row
+    return v
+
+
+def test_reconstruct_validation():
+    R = L.bitdelta_reconstruct
+
+    def call(w=FAKE, d_out=64, d_in=64, var=None, out=FAKE + 1024 * 1024):
+        v = _variant() if var is None else var
+        return R(w, d_out, d_in, ctypes.byref(v), out, None)
+
+    assert call(w=None) == INVALID
+    assert call(out=None) == INVALID
+    assert R(FAKE, 64, 64, None, FAKE, None) == INVALID
+    assert call(var=_variant(words=None)) == INVALID
+    assert call(var=_variant(alpha=None)) == INVALID
+    assert call(var=_variant(per_row=3)) == INVALID
+    assert call(d_out=0) == INVALID
+    assert call(d_in=48) == SHAPE
+    assert call(var=_variant(words=None, tiled=FAKE)) == SHAPE      # tiled needs d_in % 128
+    assert call(w=FAKE + 8) == ALIGN
+    assert call(out=FAKE + 8) == ALIGN
+    assert call(var=_variant(words=FAKE + 2)) == ALIGN
+    assert call(d_in=128, var=_variant(words=None, tiled=FAKE + 4)) == ALIGN
+
+
+def test_upload_validation():
+    U = L.bitdelta_upload_variant
+    host = np.zeros(64 * 128 // 32, dtype=np.uint32)
+    ha = np.zeros(64, dtype=np.float32)
+    hp, ap = host.ctypes.data, ha.ctypes.data
+
+    def call(hw=hp, hal=ap, na=1, d_out=64, d_in=128, words=FAKE, tiled=None, alpha=FAKE,
+             staging=None, sb=0):
+        return U(hw, hal, na, d_out, d_in, words, tiled, alpha, staging, sb, None)
+
+    assert call(hw=None) == INVALID
+    assert call(hal=None) == INVALID
+    assert call(alpha=None) == INVALID
+    assert call(words=None) == INVALID                 # no destination
+    assert call(na=2) == INVALID                       # 1 or d_out scales
+    assert call(d_out=0) == INVALID
+    assert call(d_in=48) == SHAPE
+    assert call(d_in=96, tiled=FAKE) == SHAPE
+    assert call(words=None, tiled=FAKE) == WORKSPACE   # tiled alone needs staging
+    assert call(words=None, tiled=FAKE, staging=FAKE, sb=64 * 128 // 8 - 1) == WORKSPACE
+    assert call(words=None, tiled=FAKE, staging=FAKE + 4, sb=64 * 128 // 8) == ALIGN
+    assert call(tiled=FAKE + 8) == ALIGN
+    assert call(words=FAKE + 4, tiled=FAKE) == ALIGN   # read back 16 bytes at a time
+    assert call(words=FAKE + 2) == ALIGN
+    assert call(alpha=FAKE + 2) == ALIGN

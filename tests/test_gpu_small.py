@@ -476,3 +476,28 @@ def test_split_k_pieces_grouped():
     for (_, _, y, _), y_ref in zip(probs, refs):
         rel = row_rel_l2(y.cpu().numpy().astype(np.float64), y_ref)
         assert rel.max() <= 5e-3, f"row rel L2 {rel.max():.3e}"
+
+
+def test_split_k_pieces_meet_on_one_xcd():
+    """The split K ranges of one row block are scheduled onto one XCD; the kernel checks the XCD
+    each piece ran on (hardware register) and counts in the workspace's statistics word every
+    handoff whose pieces ran on several XCDs (made coherent with a device-scope acquire).  With
+    the dispatch the schedule assumes, that count stays zero; the result matches the oracle
+    either way."""
+    d_out, d_in, m, nv = 1000, 16384, 17, 3
+    c = WL.linear_case(seed=d_out + d_in + m, d_out=d_out, d_in=d_in, m=m, num_variants=nv,
+                       dist="uniform", base_frac=0.1, zero_frac=0.01)
+    perm, offs, segv = bd.plan_segments(c["token_variant"], nv)
+    var_gpu = gpu_compress(c["deltas"])
+    w, x = bf16_dev(c["w"]), bf16_dev(c["x"][perm])
+    need = bd.matmul_workspace_bytes(m, d_in, "split")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y = bd.matmul(x, w, var_gpu, offs, segv, out_dtype="f32", path="split", workspace=ws)
+    torch.cuda.synchronize()
+    stats = ws[need - 256:need - 252].view(torch.int32).item()  # one linear: its block is last
+    var_ref = [O.compress_ref(d) for d in c["deltas"]]
+    y_ref = O.matmul_ref(O.bf16_bits_to_f64(c["x"])[perm], O.bf16_bits_to_f64(c["w"]), var_ref,
+                         offs, segv)
+    assert row_rel_l2(y.cpu().numpy().astype(np.float64), y_ref).max() <= 5e-3
+    print(f"  split handoffs across XCDs: {stats}", flush=True)
+    assert stats == 0

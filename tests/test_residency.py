@@ -35,6 +35,30 @@ def test_oracle_hand_trace():
         c.load_done(0)
 
 
+def test_oracle_hand_trace_holds():
+    # 3 variants of 10 bytes, room for 2, nothing pinned
+    c = R.ResidencyRef([10, 10, 10], 20, num_pinned=0)
+    assert c.request(0, hold=True) == (R.LOAD, [])  # a batch needs 0, then 1
+    c.load_done(0)
+    assert c.request(1, hold=True) == (R.LOAD, [])
+    c.load_done(1)
+    # 0 is the least recent, but held: without the hold it would go; now 1 is held too
+    assert c.request(2) == (R.NO_ROOM, [])
+    c.release(1)
+    assert c.request(2) == (R.LOAD, [1])            # the only unheld resident one goes
+    c.load_done(2)
+    assert c.request(2, hold=True) == (R.HIT, [])   # a hit holds too
+    assert c.request(1) == (R.NO_ROOM, [])          # 0 and 2 are both held
+    assert c.holds == [1, 0, 1]
+    c.release(0)
+    assert c.request(1) == (R.LOAD, [0])            # 0 released: the least recent unheld goes
+    assert c.holds == [0, 0, 1]
+    assert c.request(1, hold=True) == (R.QUEUED, [])  # queued behind the load, and held
+    assert c.holds == [0, 1, 1]
+    with pytest.raises(ValueError):
+        c.release(0)
+
+
 def test_oracle_pins_follow_traffic():
     c = R.ResidencyRef([5] * 6, 10, num_pinned=2)
     for v in (4, 4, 4, 2, 2, 5):
@@ -85,9 +109,12 @@ def test_oracle_invariants(seed):
 bd = pytest.importorskip("tenant_serving_bitdelta_amd")
 
 
-@pytest.mark.parametrize("seed,n,pinned,frac", [(0, 14, 6, 0.6), (1, 14, 6, 0.45), (2, 5, 1, 0.5),
-                                                (3, 64, 6, 0.3), (4, 14, 0, 0.5), (5, 3, 6, 0.9)])
-def test_manager_matches_oracle(seed, n, pinned, frac):
+@pytest.mark.parametrize("seed,n,pinned,frac,hold", [(0, 14, 6, 0.6, 0), (1, 14, 6, 0.45, 0),
+                                                     (2, 5, 1, 0.5, 0), (3, 64, 6, 0.3, 0),
+                                                     (4, 14, 0, 0.5, 0), (5, 3, 6, 0.9, 0),
+                                                     (6, 14, 6, 0.6, 1), (7, 14, 0, 0.45, 1),
+                                                     (8, 64, 6, 0.3, 1)])
+def test_manager_matches_oracle(seed, n, pinned, frac, hold):
     rng = np.random.default_rng(200 + seed)
     sizes = [int(s) for s in rng.integers(1, 9, size=n) * 1_000_000_007]  # > 2^32 in total
     cap = max(int(sum(sizes) * frac), max(sizes))
@@ -95,8 +122,15 @@ def test_manager_matches_oracle(seed, n, pinned, frac):
     lib = bd.Residency(sizes, cap, num_pinned=pinned)
     trace, coin = _random_trace(seed, n, 4000)
     for step, (v, u) in enumerate(zip(trace, coin)):
-        got, want = lib.request(int(v)), ref.request(int(v))
+        h = bool(hold) and rng.random() < 0.5
+        got, want = lib.request(int(v), hold=h), ref.request(int(v), hold=h)
         assert got == (want[0], want[1]), (step, got, want)
+        # held requests finish (release) at random later points
+        for w in range(n):
+            while ref.holds[w] and rng.random() < 0.3:
+                ref.release(w)
+                lib.release(w)
+        assert [lib.holds(w) for w in range(n)] == ref.holds, step
         # a random subset of the loads in flight finishes
         for w in range(n):
             if ref.state[w] == R.LOADING and rng.random() < u:
@@ -104,6 +138,21 @@ def test_manager_matches_oracle(seed, n, pinned, frac):
                 lib.load_done(w)
         assert [lib.state(w) for w in range(n)] == ref.state, step
         assert lib.used_bytes() == ref.used()
+
+
+def test_manager_holds_errors():
+    r = bd.Residency([10, 10, 10], 20, num_pinned=0)
+    with pytest.raises(bd.BitDeltaError):
+        r.release(0)                                     # no holder
+    assert r.request(0, hold=True) == (bd.Residency.LOAD, [])
+    r.load_done(0)
+    assert r.request(1, hold=True) == (bd.Residency.LOAD, [])
+    r.load_done(1)
+    assert r.request(2) == (bd.Residency.NO_ROOM, [])    # both residents held
+    r.release(0)
+    assert r.holds(0) == 0 and r.holds(1) == 1
+    assert r.request(2) == (bd.Residency.LOAD, [0])
+    assert r.holds(7) == -1
 
 
 def test_manager_argument_errors():
