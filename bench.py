@@ -8,9 +8,13 @@ Laplace(0, b) deltas drawn per matrix and discarded), then a step is one decode 
 segment plan plus one grouped fused reconstruct-and-multiply launch per block over its seven
 linears (independent synthetic activations per linear).
 
-Prints ONE JSON line on stdout; progress goes to stderr.
-Other workloads (--config): 2 = one down_proj GEMV (1 token, 1 variant), 3 = one block with a
-64-token uniform batch, 4 = prefill of gate and up with 4 requests x 2048 tokens.
+Prints ONE JSON line on stdout; progress goes to stderr.  The default run also measures, after
+the headline and reported under "sub_results", the other workloads with their own rooflines:
+one down_proj GEMV (1 token, 1 variant; weights rotated over copies that together exceed the
+memory-side cache), one block with a 64-token uniform batch, the prefill of gate and up with
+4 requests x 2048 tokens on 4 of 14 variants, the unfused comparison (W_eff written to HBM,
+then a plain product) for the last two, and a device-to-device copy as the measured bandwidth
+ceiling.  --config N runs one workload alone (2, 3, 4 or 5).
 """
 from __future__ import annotations
 
@@ -41,8 +45,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=5, choices=(2, 3, 4, 5))
+    p.add_argument("--config", type=int, default=None, choices=(2, 3, 4, 5),
+                   help="run one workload alone (default: the headline plus every sub-result)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sub", action="store_true", help="default run: the headline only")
+    p.add_argument("--unfused", action="store_true",
+                   help="--config 3 or 4: also time the unfused comparison")
     p.add_argument("--path", default="auto", choices=("auto", "gemv", "stream", "split", "prefill"),
                    help="decode kernel family (auto: what the library picks)")
     p.add_argument("--alpha-rows", action="store_true",
@@ -130,18 +138,20 @@ def build_layers(torch, bd, config, blocks, linears, scales, compress_timer, nva
                 delta = WL.gpu_laplace_f32(torch, (d_out, d_in), scales[v],
                                            WL.substream_seed(config, b, name, v, "delta"),
                                            out=dbuf[:d_out * d_in])
-                words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device=dev)
-                alpha = torch.empty(d_out if alpha_rows else 1, dtype=torch.float32, device=dev)
+                # one resident layout per variant: the tiled words the kernels stream (the
+                # row-major words only where d_in % 128 != 0)
                 nt = bd.sign_words_t128(d_out, d_in)
                 tiled = torch.empty(nt, dtype=torch.int32, device=dev) if nt > 0 else None
+                words = (None if tiled is not None else
+                         torch.empty((d_out, d_in // 32), dtype=torch.int32, device=dev))
+                alpha = torch.empty(d_out if alpha_rows else 1, dtype=torch.float32, device=dev)
                 compress_timer.start()
                 if alpha_rows:
                     bd.compress_rows(delta, words, alpha, workspace=ws, tiled=tiled)
                 else:
                     bd.compress(delta, words, alpha, workspace=ws, tiled=tiled)
-                # reads Delta once, writes the row-major words, the tiled copy and alpha
-                compress_timer.stop(4 * d_out * d_in + (2 if nt > 0 else 1) * (d_out * d_in // 8) +
-                                    4 * alpha.numel())
+                # reads Delta once, writes the sign words (one layout) and alpha
+                compress_timer.stop(4 * d_out * d_in + d_out * d_in // 8 + 4 * alpha.numel())
                 L.variants.append((words, alpha, tiled))
             blk.append(L)
         layers.append(blk)
@@ -185,13 +195,13 @@ class EventTimer:
 def measure_compress_pair(torch, bd, reps=5):
     """Compress from a (fine-tuned, base) bf16 pair at the gate / up shape (28672 x 8192): the
     task vector is never formed.  Algorithmic bytes: both matrices read (2 x 2 B per element),
-    the row-major words and the tiled copy written (n / 8 each) and alpha."""
+    the sign words written in the kernels' (tiled) layout (n / 8) and alpha."""
     d_out, d_in = 28672, 8192
     base = WL.gpu_normal_bf16(torch, (d_out, d_in), 0.02, WL.substream_seed(6, 0, "gate", "w"))
     delta = WL.gpu_laplace_f32(torch, (d_out, d_in), 3e-4, WL.substream_seed(6, 0, "gate", 0, "delta"))
     ft = (base.float() + delta).to(torch.bfloat16)
     del delta
-    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    words = None
     alpha = torch.empty(1, dtype=torch.float32, device="cuda")
     tiled = torch.empty(bd.sign_words_t128(d_out, d_in), dtype=torch.int32, device="cuda")
     ws = torch.empty(max(bd.compress_workspace_bytes(d_out, d_in), 8) // 8, dtype=torch.float64,
@@ -203,7 +213,7 @@ def measure_compress_pair(torch, bd, reps=5):
     for _ in range(reps):
         t.start()
         bd.compress_from_weights(ft, base, words, alpha, workspace=ws, tiled=tiled)
-        t.stop(4 * n + 2 * (n // 8) + 4)
+        t.stop(4 * n + n // 8 + 4)
     ms = t.total_ms() / reps
     gbs = t.bytes / reps / (ms / 1e3) / 1e9
     del base, ft, words, tiled, ws
@@ -212,11 +222,11 @@ def measure_compress_pair(torch, bd, reps=5):
 
 def measure_compress_rows(torch, bd, reps=5):
     """Compress with one alpha per output row at the gate / up shape (28672 x 8192).
-    Algorithmic bytes: Delta read (4 B per element), the row-major words and the tiled copy
-    written (n / 8 each) and the d_out alphas."""
+    Algorithmic bytes: Delta read (4 B per element), the sign words written in the kernels'
+    (tiled) layout (n / 8) and the d_out alphas."""
     d_out, d_in = 28672, 8192
     delta = WL.gpu_laplace_f32(torch, (d_out, d_in), 3e-4, WL.substream_seed(6, 0, "gate", 0, "delta"))
-    words = torch.empty((d_out, d_in // 32), dtype=torch.int32, device="cuda")
+    words = None
     alpha = torch.empty(d_out, dtype=torch.float32, device="cuda")
     tiled = torch.empty(bd.sign_words_t128(d_out, d_in), dtype=torch.int32, device="cuda")
     ws = torch.empty(max(bd.compress_rows_workspace_bytes(d_out, d_in), 8) // 8,
@@ -228,7 +238,7 @@ def measure_compress_rows(torch, bd, reps=5):
     for _ in range(reps):
         t.start()
         bd.compress_rows(delta, words, alpha, workspace=ws, tiled=tiled)
-        t.stop(4 * n + 2 * (n // 8) + 4 * d_out)
+        t.stop(4 * n + n // 8 + 4 * d_out)
     ms = t.total_ms() / reps
     gbs = t.bytes / reps / (ms / 1e3) / 1e9
     del delta, words, tiled, ws
@@ -259,6 +269,63 @@ def measure_delta_upload(torch, reps=3):
     del host, dev
     return {"source": "pinned host memory over PCIe", "bytes_per_copy": nbytes, "gbs": gbs,
             "variant_bytes_70b": variant, "variant_ms": variant / (gbs * 1e9) * 1e3}
+
+
+def measure_unfused(torch, bd, blk, offs, segv, path, steps, warmup):
+    """The unfused comparison the post argues against ("Serving architecture": W_eff materialised
+    in HBM against the fused kernel's bandwidth): for every linear and every variant segment of
+    the batch, W_eff = bf16(W_base + alpha * sign) is written to HBM (bitdelta_reconstruct) and
+    the segment's tokens are multiplied with it as a plain product (the base-model segment of
+    bitdelta_matmul, W_eff given as the weights); base-model tokens use W_base directly.
+    Algorithmic bytes per variant segment and linear: W_base and the sign words read and W_eff
+    written (2n + n/8 + 2n), W_eff read again (2n), the segment's activations and outputs."""
+    weff = {L.name: torch.empty((L.d_out, L.d_in), dtype=torch.bfloat16, device="cuda") for L in blk}
+    m = int(offs[-1])
+    ws = torch.empty(max(max(bd.matmul_workspace_bytes(m, L.d_in, path) for L in blk), 256),
+                     dtype=torch.uint8, device="cuda")
+    nbytes = 0
+    for L in blk:
+        n = L.d_out * L.d_in
+        for s_i, v in enumerate(segv):
+            ln = int(offs[s_i + 1] - offs[s_i])
+            nbytes += (2 * n + n // 8 + 4 + 2 * n if v >= 0 else 0) + 2 * n + 2 * ln * (L.d_in + L.d_out)
+
+    def step():
+        for L in blk:
+            for s_i, v in enumerate(segv):
+                lo, hi = int(offs[s_i]), int(offs[s_i + 1])
+                w = L.w
+                if v >= 0:
+                    w = bd.reconstruct(L.w, L.variants[int(v)], w_eff=weff[L.name])
+                bd.matmul(L.x[lo:hi], w, [], [0, hi - lo], [-1], y=L.y[lo:hi], path=path,
+                          workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    base_bytes = sum(2 * L.d_out * L.d_in for L in blk)
+    del weff, ws
+    return {"ms_per_step": ms, "tokens_per_s": m * 1e3 / ms, "bytes_per_step": nbytes,
+            "gbs": nbytes / (ms / 1e3) / 1e9, "bytes_over_base_weights": nbytes / base_bytes,
+            "launches_per_step": sum(len(segv) + int(np.sum(segv >= 0)) for _ in blk)}
+
+
+def measure_unfused_decode(args, torch, bd, blk, ids, nvar, m, fused_launch_ms):
+    _, offs, segv = bd.plan_segments(ids, nvar)
+    r = measure_unfused(torch, bd, blk, offs, segv, args.path, max(3, args.steps // 4), 1)
+    n_active = int(np.sum(segv >= 0))
+    fused_bytes = decode_bytes(blk, m, n_active)
+    r.update({"fused_ms_per_step": fused_launch_ms, "unfused_over_fused_time": r["ms_per_step"] / fused_launch_ms,
+              "fused_bytes_per_step": fused_bytes,
+              "fused_bytes_over_base_weights": fused_bytes / sum(2 * L.d_out * L.d_in for L in blk)})
+    return r
 
 
 def decode_bytes(blk, m, n_active, alpha_rows=False):
@@ -299,8 +366,9 @@ def cpu_baseline_decode(torch, config, linears_sample, scales, perm, offs, segv,
         elems += d_out * d_in
         log(f"[cpu baseline] oracle on {name} ({d_out}x{d_in}): {elapsed:.1f}s so far")
     est_step = elapsed * total_elems / elems
-    return {"value": m / est_step, "unit": "tokens/s", "cores": int(blas_threads),
-            "kind": "oracle",
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": m / est_step, "unit": "tokens/s", "cores": int(cores),
+            "blas_threads": int(blas_threads), "extrapolated": True, "kind": "oracle",
             "sample": (f"oracle matmul of block 0's {'+'.join(n for n, _, _ in linears_sample)} "
                        f"({elems} weights, all {m} tokens, {nvar} variant(s)) in {elapsed:.1f}s on the host, "
                        f"scaled by weight count to the full step ({total_elems} weights); "
@@ -309,7 +377,7 @@ def cpu_baseline_decode(torch, config, linears_sample, scales, perm, offs, segv,
 
 # ---------------------------------------------------------------------------------------------
 
-def run_decode(args, torch, bd, config):
+def run_decode(args, torch, bd, config, cpu_baseline=True, rotate=1, unfused=False):
     if config == 5:
         blocks, m, dist = 20, 256, "zipf"
         linears = list(WL.BLOCK_LINEARS)
@@ -330,6 +398,18 @@ def run_decode(args, torch, bd, config):
     layers = build_layers(torch, bd, config, blocks, linears, scales, comp, nvar,
                           alpha_rows=args.alpha_rows)
     comp_ms = comp.total_ms()
+    if rotate > 1:
+        # copies of the block (weights and sign words) in distinct memory, so consecutive steps
+        # never find their weights in the memory-side cache
+        base = layers[0]
+        for _ in range(rotate - 1):
+            blk = []
+            for L in base:
+                C = Linear(L.name, L.d_out, L.d_in)
+                C.w = L.w.clone()
+                C.variants = [tuple(None if t is None else t.clone() for t in v) for v in L.variants]
+                blk.append(C)
+            layers.append(blk)
     for b, blk in enumerate(layers):
         for L in blk:
             L.x = WL.gpu_normal_bf16(torch, (m, L.d_in), 1.0, WL.substream_seed(config, b, L.name, "x"))
@@ -339,16 +419,20 @@ def run_decode(args, torch, bd, config):
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
+    step_blocks = [layers] if rotate == 1 else [[blk] for blk in layers]
+    step_no = [0]
+
     def step(timer=None):
         # plan (host) + one grouped call per block (split path: activation prologue + main kernel)
         _, o, s = bd.plan_segments(ids, nvar)
-        for blk in layers:
+        for blk in step_blocks[step_no[0] % len(step_blocks)]:
             probs = [(L.x, L.w, L.y, L.variants) for L in blk]
             if timer:
                 timer.start()
             bd.matmul_grouped(probs, o, s, path=args.path, workspace=ws)
             if timer:
                 timer.stop()
+        step_no[0] += 1
 
     for _ in range(args.warmup):
         step()
@@ -366,7 +450,7 @@ def run_decode(args, torch, bd, config):
     bytes_launch = decode_bytes(layers[0], m, n_active, args.alpha_rows)  # every block has the same shapes
     avg_launch_s = kern_ms / launches / 1e3
     achieved = bytes_launch / avg_launch_s / 1e9
-    total_elems = sum(L.d_out * L.d_in for blk in layers for L in blk)
+    total_elems = sum(L.d_out * L.d_in for blk in step_blocks[0] for L in blk)
     path = bd.auto_path(m, offs, segv) if args.path == "auto" else bd.PATHS[args.path]
     if args.alpha_rows and path == 4:
         path = 2  # per-row scales: the library runs the batch on the streaming kernel
@@ -374,9 +458,13 @@ def run_decode(args, torch, bd, config):
     pair = measure_compress_pair(torch, bd) if config == 5 else None
     rows = measure_compress_rows(torch, bd) if config == 5 else None
     upload = measure_delta_upload(torch) if config == 5 else None
+    unf = (measure_unfused_decode(args, torch, bd, layers[0], ids, nvar, m, kern_ms / launches)
+           if unfused else None)
+    resident_sign_bytes = sum(int(t.numel()) * 4 for blk in step_blocks[0] for L in blk
+                              for v in L.variants for t in (v[0], v[2]) if t is not None)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_baseline and not args.no_cpu_baseline:
         sample = [l for l in linears if l[0] in ("q", "k", "v", "o", "gate")] or linears
         cpu = cpu_baseline_decode(torch, config, sample, scales, perm, offs, segv, m, total_elems,
                                   nvar)
@@ -399,6 +487,8 @@ def run_decode(args, torch, bd, config):
                    "segments": [int(v) for v in np.diff(offs)], "active_variants": n_active,
                    "launches_per_step": launches // args.steps,
                    "kernel_path": {1: "gemv", 2: "stream", 3: "prefill", 4: "split"}[path],
+                   "weight_copies_rotated": rotate,
+                   "resident_sign_bytes": resident_sign_bytes,
                    "parallelism": "single GPU"},
         "hbm_gbs_step": bytes_launch * len(layers) / (ms_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -413,11 +503,12 @@ def run_decode(args, torch, bd, config):
         "compress_from_weights": pair,
         "compress_rows": rows,
         "delta_upload": upload,
+        "unfused": unf,
         "cpu_baseline": cpu,
     }
 
 
-def run_prefill(args, torch, bd):
+def run_prefill(args, torch, bd, unfused=False):
     config = 4
     linears = [("gate", 28672, 8192), ("up", 28672, 8192)]
     scales = WL.decode_variant_scales(config)
@@ -455,6 +546,11 @@ def run_prefill(args, torch, bd):
     kern_ms = kt.total_ms() / len(kt.pairs)
     flops = sum(2.0 * m * L.d_out * L.d_in for L in layers)
     achieved = flops / (kern_ms / 1e3) / 1e12
+    unf = None
+    if unfused:
+        unf = measure_unfused(torch, bd, layers, offs, segv, "prefill", max(2, args.steps // 4), 1)
+        unf.update({"fused_ms_per_step": kern_ms, "unfused_over_fused_time": unf["ms_per_step"] / kern_ms,
+                    "tflops_unfused": flops / (unf["ms_per_step"] / 1e3) / 1e12})
     return {
         "metric": "fused BitDelta matmul tokens/s (prefill, bf16 MFMA), 14 variants resident",
         "value": m * 1e3 / ms_step, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -467,6 +563,7 @@ def run_prefill(args, torch, bd):
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "prefill_kernel", "flops_per_launch": flops,
                      "avg_launch_us": kern_ms * 1e3},
+        "unfused": unf,
         "cpu_baseline": None,
     }
 
@@ -488,10 +585,75 @@ def main():
         print(json.dumps(copy_calibration(torch)), flush=True)
         return
     if args.config == 4:
-        res = run_prefill(args, torch, bd)
+        res = run_prefill(args, torch, bd, unfused=args.unfused)
+    elif args.config is not None:
+        res = run_decode(args, torch, bd, args.config, rotate=4 if args.config == 2 else 1,
+                         unfused=args.unfused and args.config == 3)
     else:
-        res = run_decode(args, torch, bd, args.config)
+        res = run_decode(args, torch, bd, 5)
+        if not args.no_sub:
+            res["sub_results"] = sub_results(args, torch, bd, res)
     print(json.dumps(res), flush=True)
+
+
+def _sub(r):
+    """The fields of a workload's result that the headline line carries for it."""
+    keep = ("value", "unit", "ms_per_step", "dtype", "unfused")
+    d = {k: r[k] for k in keep if k in r}
+    d["workload"] = r["config"]["workload"]
+    d["config_index"] = r["config"]["config_index"]
+    d["roofline"] = {k: r["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                                   "kernel", "avg_launch_us") if k in r["roofline"]}
+    return d
+
+
+def measure_copy_ceiling(torch, reps=5):
+    """Device-to-device copy of a 2 GiB buffer (hipMemcpyAsync): bytes read + written per second,
+    the bandwidth a plain copy reaches on this GPU."""
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"what": "device-to-device copy of 2 GiB (hipMemcpyAsync), read + write bytes",
+            "gbs": 2 * n / (ms / 1e3) / 1e9, "ms": ms}
+
+
+def sub_results(args, torch, bd, head):
+    """The other workloads, each with its own roofline, measured after the headline (its memory
+    freed first)."""
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    out = {}
+    steps = max(4, args.steps // 2)
+    sub_args = argparse.Namespace(**vars(args))
+    sub_args.steps, sub_args.warmup = steps, max(1, args.warmup)
+    log("[sub] copy ceiling")
+    ceil = measure_copy_ceiling(torch)
+    out["copy_ceiling"] = ceil
+    head["roofline"]["frac_of_copy_ceiling"] = head["roofline"]["achieved"] / ceil["gbs"]
+    log("[sub] config 2: GEMV, 1 token, weights rotated over 4 copies")
+    out["gemv_1tok"] = _sub(run_decode(sub_args, torch, bd, 2, cpu_baseline=False, rotate=4))
+    gc.collect()
+    torch.cuda.empty_cache()
+    log("[sub] config 3: one block, 64 tokens, with the unfused comparison")
+    out["block_64tok"] = _sub(run_decode(sub_args, torch, bd, 3, cpu_baseline=False, unfused=True))
+    gc.collect()
+    torch.cuda.empty_cache()
+    log("[sub] config 4: prefill, with the unfused comparison")
+    out["prefill_4x2048"] = _sub(run_prefill(sub_args, torch, bd, unfused=True))
+    for k in ("gemv_1tok", "block_64tok"):
+        out[k]["roofline"]["frac_of_copy_ceiling"] = out[k]["roofline"]["achieved"] / ceil["gbs"]
+    return out
 
 
 if __name__ == "__main__":

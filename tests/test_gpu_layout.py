@@ -75,12 +75,17 @@ def test_tiled_only_variants(case):
     y_ref = O.matmul_ref(xf, O.bf16_bits_to_f64(c["w"]), var_ref, offs, segv)
     y_delta = oracle_delta_term(xf, var_ref, offs, segv, d_out, d_in)
     for path in paths:
+        # the kernel family that runs (AUTO picks by batch size)
+        eff = path if path != "auto" else {1: "gemv", 2: "stream", 3: "prefill", 4: "split"}[
+            bd.auto_path(m, offs, segv)]
         for out in ("bf16", "f32"):
             y_t = bd.matmul(x, w, tiled_only, offs, segv, out_dtype=out, path=path)
             got = y_t.float().cpu().numpy().astype(np.float64)
             assert row_rel_l2(got, y_ref).max() <= ROW_L2_TOL, (path, out)
             dres = delta_residual(got, y_ref, y_delta)
-            lim = DELTA_RESIDUAL_TOL_BF16 if out == "bf16" else (0.75 if path == "prefill" else 1e-2)
+            # fp32 output: prefill rounds W_eff to bf16 (the delta term then carries that
+            # rounding); the other paths keep it to fp32 or 8 significant bits
+            lim = DELTA_RESIDUAL_TOL_BF16 if out == "bf16" else (0.75 if eff == "prefill" else 1e-2)
             assert dres.max() <= lim, (path, out, float(dres.max()))
             if path in ("gemv", "stream", "prefill"):
                 # the layout changes only where the words are read from: the same bits
