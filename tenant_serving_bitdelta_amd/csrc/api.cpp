@@ -28,9 +28,31 @@ struct Segment {
   int begin, len, variant;
 };
 
+// The non-empty segments of a call (at most BITDELTA_MAX_SEGMENTS), in a fixed array so that
+// planning allocates no memory.
+struct SegList {
+  Segment s[BITDELTA_MAX_SEGMENTS];
+  int n = 0;
+  const Segment* begin() const { return s; }
+  const Segment* end() const { return s + n; }
+  void push_back(const Segment& x) { s[n++] = x; }
+  bool empty() const { return n == 0; }
+};
+
+// Variant of token t (a position of the batch in segment order); segments are sorted by begin.
+int variant_at(const SegList& segs, int t) {
+  int lo = 0, hi = segs.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (segs.s[mid].begin <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return segs.s[lo].variant;
+}
+
 // Validates the shared segmentation; drops empty segments.
 bitdelta_status check_segments(int64_t M, const int32_t* seg_offsets, const int32_t* seg_variant,
-                               int32_t num_segments, std::vector<Segment>* out) {
+                               int32_t num_segments, SegList* out) {
   if (M < 0 || M >= kMaxDim) return BITDELTA_ERR_INVALID_ARG;
   if (num_segments < 0 || num_segments > BITDELTA_MAX_SEGMENTS) return BITDELTA_ERR_INVALID_ARG;
   if (M == 0 && num_segments == 0) return BITDELTA_OK;
@@ -46,8 +68,7 @@ bitdelta_status check_segments(int64_t M, const int32_t* seg_offsets, const int3
   return BITDELTA_OK;
 }
 
-bitdelta_status check_problem(const bitdelta_problem& p, int64_t M,
-                              const std::vector<Segment>& segs) {
+bitdelta_status check_problem(const bitdelta_problem& p, int64_t M, const SegList& segs) {
   // an empty batch may come with empty (null) activation and output buffers
   if (!p.w_base || (M > 0 && (!p.x || !p.y))) return BITDELTA_ERR_INVALID_ARG;
   if (p.d_out <= 0 || p.d_in <= 0 || p.d_out >= kMaxDim || p.d_in >= kMaxDim)
@@ -93,7 +114,7 @@ size_t workspace_for(int64_t M, int64_t d_in, int path) {
 
 // The streaming kernels read sign words 16 bytes (4 K steps) per row at a time: the tiled
 // layout, or 16-byte aligned row-major words.
-bool stream_eligible(const bitdelta_problem* probs, int np, const std::vector<Segment>& segs) {
+bool stream_eligible(const bitdelta_problem* probs, int np, const SegList& segs) {
   for (int p = 0; p < np; ++p) {
     if (probs[p].d_in % 128 != 0) return false;
     for (const Segment& s : segs) {
@@ -107,8 +128,7 @@ bool stream_eligible(const bitdelta_problem* probs, int np, const std::vector<Se
 
 // The split path reads the tiled sign words and addresses its activation layouts and the tiled
 // words with 31-bit offsets.
-bool split_eligible(const bitdelta_problem* probs, int np, int64_t M,
-                    const std::vector<Segment>& segs) {
+bool split_eligible(const bitdelta_problem* probs, int np, int64_t M, const SegList& segs) {
   for (int p = 0; p < np; ++p) {
     const bitdelta_problem& P = probs[p];
     if (P.d_in % 128 != 0) return false;
@@ -125,8 +145,8 @@ bool split_eligible(const bitdelta_problem* probs, int np, int64_t M,
 }
 
 // ---- GEMV: one launch per linear ----------------------------------------------------------
-bitdelta_status run_gemv(const bitdelta_problem* probs, int np, int64_t M,
-                         const std::vector<Segment>& segs, int y_f32, hipStream_t st) {
+bitdelta_status run_gemv(const bitdelta_problem* probs, int np, int64_t M, const SegList& segs,
+                         int y_f32, hipStream_t st) {
   for (int p = 0; p < np; ++p) {
     const bitdelta_problem& P = probs[p];
     bd::GemvArgs a;
@@ -166,8 +186,8 @@ struct Tile {
   int row, valid, variant;
 };
 
-bitdelta_status run_stream(const bitdelta_problem* probs, int np,
-                           const std::vector<Segment>& segs, int y_f32, hipStream_t st) {
+bitdelta_status run_stream(const bitdelta_problem* probs, int np, const SegList& segs, int y_f32,
+                           hipStream_t st) {
   std::vector<Tile> tiles;
   for (const Segment& s : segs)
     for (int r = 0; r < s.len; r += 16) tiles.push_back({s.begin + r, s.len - r < 16 ? s.len - r : 16, s.variant});
@@ -254,8 +274,8 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np,
 // tokens that would give a wave more than kSplitMaxGroups groups.  The less loaded wave of each
 // SIMD issues that SIMD's share of the global->LDS copies.
 struct SplitPlan {
-  int t_begin = 0, t_end = 0, tok_base = 0, nd = 1, ng = 0;
-  std::vector<int> slot_var;
+  int t_begin = 0, t_end = 0, tok_base = 0, nd = 1, ng = 0, nslot = 0;
+  int slot_var[bd::kMaxSlots];
   bd::SplitWave wv[8];
   int8_t token_slot[bd::kSplitMaxM];
 };
@@ -264,28 +284,30 @@ struct SplitPlan {
 // pair (16 fp4 x fp6 MFMAs and the lane masking) and one expansion of a variant's sign words.
 constexpr int kCostTile = 512, kCostPair = 320, kCostExpand = 224;
 
-bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* pl) {
+bool plan_split(const SegList& segs, int t_begin, int t_end, SplitPlan* pl) {
   const int tok_base = t_begin / 16 * 16;
   const int ntiles = (t_end - 1 - tok_base) / 16 + 1;
   if (ntiles > bd::kSplitMaxM / 16) return false;
-  std::vector<int> slot_var;
+  int slot_var[bd::kMaxSlots];
+  int nslot = 0;
   int8_t token_slot[bd::kSplitMaxM];
   memset(token_slot, -1, sizeof(token_slot));
   for (int t = t_begin; t < t_end; ++t) {
-    if (tv[t] < 0) continue;
+    const int v = variant_at(segs, t);
+    if (v < 0) continue;
     int slot = -1;
-    for (int q = 0; q < (int)slot_var.size(); ++q)
-      if (slot_var[q] == tv[t]) slot = q;
+    for (int q = 0; q < nslot; ++q)
+      if (slot_var[q] == v) slot = q;
     if (slot < 0) {
-      if ((int)slot_var.size() == bd::kMaxSlots) return false;
-      slot_var.push_back(tv[t]);
-      slot = (int)slot_var.size() - 1;
+      if (nslot == bd::kMaxSlots) return false;
+      slot_var[nslot] = v;
+      slot = nslot++;
     }
     token_slot[t - tok_base] = (int8_t)slot;
   }
   const int nd = ntiles <= 8 ? 1 : 2;
   // the distinct slots of each tile, as a bit set
-  std::vector<unsigned> tset(ntiles, 0u);
+  unsigned tset[bd::kSplitMaxM / 16] = {0u};
   for (int i = 0; i < ntiles; ++i)
     for (int t = 16 * i; t < 16 * i + 16; ++t)
       if (token_slot[t] >= 0) tset[i] |= 1u << token_slot[t];
@@ -294,7 +316,8 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
     int tile[2];
     int ngroups, cost;
   };
-  std::vector<Unit> units;
+  Unit units[bd::kSplitMaxM / 16];
+  int nunits = 0;
   for (int i = 0; i < ntiles; i += nd) {
     Unit u;
     u.tile[0] = i;
@@ -306,15 +329,22 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
     u.cost = kCostTile * (u.tile[1] >= 0 ? 2 : 1) + kCostPair * (n0 + n1) +
              kCostExpand * __builtin_popcount(s0 | s1);
     if (u.ngroups > bd::kSplitMaxGroups) return false;
-    units.push_back(u);
+    units[nunits++] = u;
   }
-  std::vector<int> order(units.size());
-  for (size_t k = 0; k < units.size(); ++k) order[k] = (int)k;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int l, int r) { return units[l].cost > units[r].cost; });
+  // units by cost, longest first (insertion sort: stable, no allocation)
+  int order[bd::kSplitMaxM / 16];
+  for (int k = 0; k < nunits; ++k) {
+    int i = k;
+    while (i > 0 && units[order[i - 1]].cost < units[k].cost) {
+      order[i] = order[i - 1];
+      --i;
+    }
+    order[i] = k;
+  }
   int simd_load[4] = {0, 0, 0, 0}, simd_waves[4] = {0, 0, 0, 0};
-  std::vector<int> wave_of(units.size(), -1);
-  for (int k : order) {
+  int wave_of[bd::kSplitMaxM / 16];
+  for (int oi = 0; oi < nunits; ++oi) {
+    const int k = order[oi];
     int best = -1;
     for (int sm = 0; sm < 4; ++sm)
       if (simd_waves[sm] < 2 && (best < 0 || simd_load[sm] < simd_load[best])) best = sm;
@@ -322,12 +352,13 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
     simd_load[best] += units[k].cost;
   }
   int wave_load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (size_t k = 0; k < units.size(); ++k) wave_load[wave_of[k]] = units[k].cost;
+  for (int k = 0; k < nunits; ++k) wave_load[wave_of[k]] = units[k].cost;
   pl->t_begin = t_begin;
   pl->t_end = t_end;
   pl->tok_base = tok_base;
   pl->nd = nd;
-  pl->slot_var = slot_var;
+  pl->nslot = nslot;
+  memcpy(pl->slot_var, slot_var, sizeof(slot_var));
   memcpy(pl->token_slot, token_slot, sizeof(token_slot));
   pl->ng = 0;
   for (int w = 0; w < 8; ++w) {
@@ -340,7 +371,7 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
   }
   for (int sm = 0; sm < 4; ++sm)
     pl->wv[wave_load[sm] < wave_load[sm + 4] ? sm : sm + 4].copier = sm;
-  for (size_t k = 0; k < units.size(); ++k) {
+  for (int k = 0; k < nunits; ++k) {
     bd::SplitWave& W = pl->wv[wave_of[k]];
     const Unit& u = units[k];
     W.tile[0] = u.tile[0];
@@ -362,13 +393,13 @@ bool plan_split(const std::vector<int>& tv, int t_begin, int t_end, SplitPlan* p
   return true;
 }
 
-bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
-                          const std::vector<Segment>& segs, int y_f32, void* workspace,
-                          hipStream_t st) {
+bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, const SegList& segs,
+                          int y_f32, void* workspace, hipStream_t st) {
   // workspace: per problem bf16 pieces, fp6 pieces, block scales; then every problem's share of
   // partial slots, then of split counters, then of statistics blocks
   const int Mp = (int)((M + 15) / 16 * 16);
-  std::vector<unsigned char*> xb(np), xq(np), xs(np), xc(np);
+  unsigned char *xb[BITDELTA_MAX_PROBLEMS], *xq[BITDELTA_MAX_PROBLEMS], *xs[BITDELTA_MAX_PROBLEMS],
+      *xc[BITDELTA_MAX_PROBLEMS];
   size_t off = 0;
   for (int p = 0; p < np; ++p) {
     unsigned char* base = static_cast<unsigned char*>(workspace) + off;
@@ -390,15 +421,17 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
   // statistics: the first word of the first problem's block (it accumulates, never cleared)
   uint32_t* stats = reinterpret_cast<uint32_t*>(after_slots + (size_t)np * bd::kSplitCounterBytes);
   const int C = bd::split_compute_units() / 8;
-  // problems with longer rows first, so the longest workgroups do not form the tail
-  std::vector<int> order(np);
-  for (int p = 0; p < np; ++p) order[p] = p;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int l, int r) { return probs[l].d_in > probs[r].d_in; });
-
-  std::vector<int> tv((size_t)M, -1);
-  for (const Segment& s : segs)
-    for (int t = s.begin; t < s.begin + s.len; ++t) tv[t] = s.variant;
+  // problems with longer rows first, so the longest workgroups do not form the tail (insertion
+  // sort: stable, no allocation)
+  int order[BITDELTA_MAX_PROBLEMS];
+  for (int p = 0; p < np; ++p) {
+    int i = p;
+    while (i > 0 && probs[order[i - 1]].d_in < probs[p].d_in) {
+      order[i] = order[i - 1];
+      --i;
+    }
+    order[i] = p;
+  }
 
   int t_begin = 0;
   while (t_begin < M) {
@@ -407,10 +440,13 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
     const int limit = (int)std::min<int64_t>(M, t_begin / 16 * 16 + bd::kSplitMaxM);
     int t = t_begin;
     while (t < limit) {
-      int e = t + 1;
-      while (e < limit && e % 16 != 0 && tv[e] == tv[t]) ++e;
+      // the run of token t: same variant (segment), same 16-token block
+      int seg_end = t + 1;
+      for (const Segment& sg : segs)
+        if (sg.begin <= t && t < sg.begin + sg.len) seg_end = sg.begin + sg.len;
+      const int e = std::min(std::min(seg_end, limit), (t / 16 + 1) * 16);
       SplitPlan cand;
-      if (!plan_split(tv, t_begin, e, &cand)) break;
+      if (!plan_split(segs, t_begin, e, &cand)) break;
       plan = cand;
       t = e;
     }
@@ -423,7 +459,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
     a.lo = plan.t_begin - plan.tok_base;
     a.hi = plan.t_end - plan.tok_base;
     a.Mp = Mp;
-    a.nslots = (int)plan.slot_var.size();
+    a.nslots = plan.nslot;
     a.y_f32 = y_f32;
     memcpy(a.wv, plan.wv, sizeof(a.wv));
     memcpy(a.token_slot, plan.token_slot, sizeof(a.token_slot));
@@ -477,7 +513,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
         S.d_out = (int)P.d_out;
         S.d_in = (int)P.d_in;
         S.nblocks = (int)((P.d_out + bd::kSplitRows - 1) / bd::kSplitRows);
-        for (int s = 0; s < (int)plan.slot_var.size(); ++s) {
+        for (int s = 0; s < plan.nslot; ++s) {
           S.words[s] = P.variants[plan.slot_var[s]].sign_words_t128;
           act.alpha[q][s] = P.variants[plan.slot_var[s]].alpha;
         }
@@ -493,8 +529,8 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M,
 }
 
 // ---- prefill: per-segment tiles of 256 tokens ---------------------------------------------
-bitdelta_status run_prefill(const bitdelta_problem* probs, int np,
-                            const std::vector<Segment>& segs, int y_f32, hipStream_t st) {
+bitdelta_status run_prefill(const bitdelta_problem* probs, int np, const SegList& segs, int y_f32,
+                            hipStream_t st) {
   struct MT {
     int row, rows, variant;
   };
@@ -766,7 +802,7 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
     return BITDELTA_ERR_INVALID_ARG;
   if (y_dtype != BITDELTA_OUT_BF16 && y_dtype != BITDELTA_OUT_F32) return BITDELTA_ERR_INVALID_ARG;
   if (path < BITDELTA_PATH_AUTO || path > BITDELTA_PATH_SPLIT) return BITDELTA_ERR_INVALID_ARG;
-  std::vector<Segment> segs;
+  SegList segs;
   bitdelta_status s = check_segments(M, seg_offsets, seg_variant, num_segments, &segs);
   if (s != BITDELTA_OK) return s;
   for (int p = 0; p < num_problems; ++p) {

@@ -16,7 +16,6 @@
 #include <functional>
 #include <mutex>
 #include <utility>
-#include <vector>
 
 #include "bd_internal.h"
 
@@ -40,6 +39,8 @@ bool same_shape(const SplitShape& a, const SplitShape& b) {
 
 // Pieces of one unit the kernel's counter can count: 6 bits per XCD field.
 constexpr int kMaxParts = 63;
+// Compute units of one XCD the dispatch simulation models at most.
+constexpr int kMaxUnitsPerXcd = 256;
 
 // list lengths, split units and partial slots of one XCD's list (the kernel's piece map); the
 // return value is the largest number of pieces of one unit
@@ -66,17 +67,18 @@ int count_pieces(const SplitShape& sh, SplitSched* h) {
 // compute units: a piece costs its steps, c_piece for filling the copy ring and storing, and
 // c_part for each partial slot it writes or (the last piece of a unit) reads.
 double simulate(const SplitShape& sh, const SplitSched& h, double c_piece, double c_part) {
-  std::vector<double> cu((size_t)sh.C, 0.0);
-  std::make_heap(cu.begin(), cu.end(), std::greater<double>());
+  double cu[kMaxUnitsPerXcd];  // a heap of the compute units' finishing times (no allocation)
+  const int C = std::max(1, std::min(sh.C, kMaxUnitsPerXcd));
+  std::fill(cu, cu + C, 0.0);
   for (int kk = 0; kk < h.nheads + h.npool; ++kk) {
     const SplitPiece pc = split_piece(h, sh.np, sh.ns, sh.nb, kk);
     double cost = (pc.k1 - pc.k0) + c_piece;
     if (pc.nparts > 1) cost += c_part * (pc.part == pc.nparts - 1 ? pc.nparts : 1);
-    std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
-    cu.back() += cost;
-    std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+    std::pop_heap(cu, cu + C, std::greater<double>());
+    cu[C - 1] += cost;
+    std::push_heap(cu, cu + C, std::greater<double>());
   }
-  return *std::max_element(cu.begin(), cu.end());
+  return *std::max_element(cu, cu + C);
 }
 
 SplitSched choose(const SplitShape& sh) {
@@ -123,18 +125,24 @@ SplitSched choose(const SplitShape& sh) {
 }  // namespace
 
 SplitSched split_schedule(const SplitShape& sh) {
-  // serving calls the same few shapes over and over: keep the recent schedules
+  // serving calls the same few shapes over and over: keep the 64 most recently computed
+  // schedules in a fixed ring (no allocation)
+  constexpr int kCache = 64;
   static std::mutex mu;
-  static std::vector<std::pair<SplitShape, SplitSched>> cache;
+  static SplitShape shapes[kCache];
+  static SplitSched scheds[kCache];
+  static int filled = 0, next = 0;
   {
     std::lock_guard<std::mutex> lk(mu);
-    for (const auto& e : cache)
-      if (same_shape(e.first, sh)) return e.second;
+    for (int i = 0; i < filled; ++i)
+      if (same_shape(shapes[i], sh)) return scheds[i];
   }
   const SplitSched c = choose(sh);
   std::lock_guard<std::mutex> lk(mu);
-  if (cache.size() >= 64) cache.erase(cache.begin());
-  cache.push_back({sh, c});
+  shapes[next] = sh;
+  scheds[next] = c;
+  next = (next + 1) % kCache;
+  if (filled < kCache) ++filled;
   return c;
 }
 
