@@ -286,6 +286,31 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
                                         int32_t y_dtype, int32_t path, void* workspace,
                                         size_t workspace_bytes, bitdelta_stream stream);
 
+/*
+ * bitdelta_matmul_grouped_noalloc — bitdelta_matmul_grouped for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the SPLIT decode path (the one whose kernels use a workspace) with that workspace
+ * in a scratch array the library holds, BITDELTA_NOALLOC_SCRATCH_BYTES per device, from the first
+ * call on a device until the process ends.  It calls no allocation routine.  The caller passes
+ * inputs and outputs as for bitdelta_matmul_grouped.
+ *
+ *   path  AUTO or SPLIT; a batch the SPLIT path does not serve (AUTO would pick GEMV or PREFILL
+ *         for this M, a variant lacks the tiled words or has per-row scales, d_in % 128 != 0)
+ *         gives UNSUPPORTED: use bitdelta_matmul_grouped for those (they need no workspace).
+ * Errors: as bitdelta_matmul_grouped, plus WORKSPACE when the batch needs more than
+ * BITDELTA_NOALLOC_SCRATCH_BYTES (the sum over the problems of
+ * bitdelta_matmul_workspace_bytes(M, d_in, BITDELTA_PATH_SPLIT)), checked before anything is
+ * enqueued.  All calls on one device share its scratch: calls that overlap in time on one device
+ * (on different streams, or from several threads) race and must not be made.  ABI 7.
+ */
+#define BITDELTA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+bitdelta_status bitdelta_matmul_grouped_noalloc(const bitdelta_problem* problems,
+                                                int32_t num_problems, int64_t M,
+                                                const int32_t* seg_offsets,
+                                                const int32_t* seg_variant, int32_t num_segments,
+                                                int32_t y_dtype, int32_t path,
+                                                bitdelta_stream stream);
+
 /* The kernel family bitdelta_matmul_grouped's AUTO picks for this batch shape (a bitdelta_path
  * value), or -1 for invalid segments.  Host only.  It sees the shape, not the variants: where it
  * answers SPLIT, a call whose variants lack the tiled sign words or d_in % 128, or that holds a

@@ -17,9 +17,11 @@ __all__ = [
     "compress_rows", "compress_rows_workspace_bytes", "compress_from_weights",
     "compress", "plan_segments", "matmul", "matmul_grouped", "auto_path", "PATHS",
     "matmul_workspace_bytes", "sign_words_t128", "reconstruct", "upload_variant", "Residency",
+    "matmul_grouped_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 ABI_VERSION = 7
+NOALLOC_SCRATCH_BYTES = 128 << 20  # BITDELTA_NOALLOC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitdelta.so")
@@ -140,6 +142,11 @@ def _lib():
                                               ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_size_t, ctypes.c_void_p]
+        L.bitdelta_matmul_grouped_noalloc.restype = ctypes.c_int
+        L.bitdelta_matmul_grouped_noalloc.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32,
+                                                      ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_void_p]
         L.bitdelta_matmul_workspace_bytes.restype = ctypes.c_size_t
         L.bitdelta_matmul_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
                                                       ctypes.c_int32]
@@ -381,17 +388,11 @@ def _variants_array(variants, d_out, d_in):
     return arr
 
 
-def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="auto", stream=None,
-                   workspace=None):
-    """Fused y = x (W_base + alpha_v sign_v)^T for several linears sharing one segmentation.
-    ``problems``: list of (x, w_base, y, variants) with variants a list of (words, alpha).
-    ``workspace``: device tensor of at least the summed matmul_workspace_bytes (allocated here
-    when None)."""
+def _problems_array(problems, m, out_dtype):
+    """ctypes array of bitdelta_problem for (x, w_base, y, variants) tuples, sizes checked; the
+    second value keeps the variant arrays alive."""
     if not 1 <= len(problems) <= MAX_PROBLEMS:
         raise ValueError("1..8 problems per call")
-    offs, offs_p = _i32(seg_offsets)
-    segv, segv_p = _i32(seg_variant)
-    m = int(offs[-1]) if offs.size else 0
     parr = (_Problem * len(problems))()
     keep = []
     for i, (x, w, y, variants) in enumerate(problems):
@@ -408,6 +409,19 @@ def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="a
         parr[i].d_out, parr[i].d_in = d_out, d_in
         parr[i].variants = ctypes.cast(varr, ctypes.POINTER(_Variant))
         parr[i].num_variants = len(variants)
+    return parr, keep
+
+
+def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="auto", stream=None,
+                   workspace=None):
+    """Fused y = x (W_base + alpha_v sign_v)^T for several linears sharing one segmentation.
+    ``problems``: list of (x, w_base, y, variants) with variants a list of (words, alpha).
+    ``workspace``: device tensor of at least the summed matmul_workspace_bytes (allocated here
+    when None)."""
+    offs, offs_p = _i32(seg_offsets)
+    segv, segv_p = _i32(seg_variant)
+    m = int(offs[-1]) if offs.size else 0
+    parr, keep = _problems_array(problems, m, out_dtype)
     # the library checks the size of a caller's workspace itself; only a missing one is sized here
     need = 0 if workspace is not None else sum(
         matmul_workspace_bytes(m, int(w.shape[1]), path) for _, w, _, _ in problems)
@@ -416,6 +430,21 @@ def matmul_grouped(problems, seg_offsets, seg_variant, out_dtype="bf16", path="a
                                           _OUT[out_dtype], PATHS[path], ws_ptr, ws_bytes,
                                           _stream(stream)),
            "bitdelta_matmul_grouped")
+    return [p[2] for p in problems]
+
+
+def matmul_grouped_noalloc(problems, seg_offsets, seg_variant, out_dtype="bf16", path="auto",
+                           stream=None):
+    """matmul_grouped on the SPLIT path with the library's own per-device scratch as workspace:
+    the call allocates no device memory (for callers that cannot).  Batches the SPLIT path does
+    not serve raise BitDeltaError (status 5); calls that overlap on one device must not be made."""
+    offs, offs_p = _i32(seg_offsets)
+    segv, segv_p = _i32(seg_variant)
+    m = int(offs[-1]) if offs.size else 0
+    parr, keep = _problems_array(problems, m, out_dtype)
+    _check(_lib().bitdelta_matmul_grouped_noalloc(parr, len(problems), m, offs_p, segv_p, segv.size,
+                                                  _OUT[out_dtype], PATHS[path], _stream(stream)),
+           "bitdelta_matmul_grouped_noalloc")
     return [p[2] for p in problems]
 
 

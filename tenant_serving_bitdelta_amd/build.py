@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitdelta.so")
 
 SOURCES = ["compress.hip", "gemv.hip", "stream.hip", "split.hip", "prefill.hip", "reconstruct.hip",
-           "split_sched.cpp", "api.cpp", "residency.cpp"]
+           "noalloc.hip", "split_sched.cpp", "api.cpp", "residency.cpp"]
 ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -597,6 +597,37 @@ bitdelta_status run_prefill(const bitdelta_problem* probs, int np, const SegList
 
 namespace bd {
 bitdelta_status status_of_hip(hipError_t e) { return map_hip(e); }
+
+// bitdelta_matmul_grouped restricted to the SPLIT path, with the workspace supplied by the
+// library (the scratch-backed entry point): every argument is checked as for the grouped call;
+// a batch the SPLIT path does not serve (AUTO would pick another path, or a variant lacks the
+// tiled words or has per-row scales) is UNSUPPORTED; a workspace need above `ws_bytes` is
+// WORKSPACE.  Nothing is enqueued on an error.
+bitdelta_status matmul_grouped_split(const bitdelta_problem* problems, int32_t num_problems,
+                                     int64_t M, const int32_t* seg_offsets,
+                                     const int32_t* seg_variant, int32_t num_segments,
+                                     int32_t y_dtype, int32_t path, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!problems || num_problems <= 0 || num_problems > BITDELTA_MAX_PROBLEMS)
+    return BITDELTA_ERR_INVALID_ARG;
+  if (y_dtype != BITDELTA_OUT_BF16 && y_dtype != BITDELTA_OUT_F32) return BITDELTA_ERR_INVALID_ARG;
+  if (path != BITDELTA_PATH_AUTO && path != BITDELTA_PATH_SPLIT) return BITDELTA_ERR_UNSUPPORTED;
+  SegList segs;
+  bitdelta_status s = check_segments(M, seg_offsets, seg_variant, num_segments, &segs);
+  if (s != BITDELTA_OK) return s;
+  for (int p = 0; p < num_problems; ++p) {
+    s = check_problem(problems[p], M, segs);
+    if (s != BITDELTA_OK) return s;
+  }
+  if (M == 0) return BITDELTA_OK;
+  if (path == BITDELTA_PATH_AUTO && pick_path(M) != BITDELTA_PATH_SPLIT) return BITDELTA_ERR_UNSUPPORTED;
+  if (!split_eligible(problems, num_problems, M, segs)) return BITDELTA_ERR_UNSUPPORTED;
+  size_t need = 0;
+  for (int p = 0; p < num_problems; ++p) need += workspace_for(M, problems[p].d_in, BITDELTA_PATH_SPLIT);
+  if (!workspace || need > ws_bytes) return BITDELTA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITDELTA_ERR_ALIGNMENT;
+  return run_split(problems, num_problems, M, segs, y_dtype == BITDELTA_OUT_F32, workspace, stream);
+}
 }  // namespace bd
 
 extern "C" {
