@@ -490,7 +490,7 @@ def run_decode(args, torch, bd, config, cpu_baseline=True, rotate=1, unfused=Fal
                    "weight_copies_rotated": rotate,
                    "resident_sign_bytes": resident_sign_bytes,
                    "parallelism": "single GPU"},
-        "hbm_gbs_step": bytes_launch * len(layers) / (ms_step / 1e3) / 1e9,
+        "hbm_gbs_step": bytes_launch * len(step_blocks[0]) / (ms_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if (config == 5 and path == 4) else None,

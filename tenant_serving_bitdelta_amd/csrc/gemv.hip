@@ -3,9 +3,9 @@
 // weight W_eff = W_base + alpha_v * sign_v formed in fp32 registers, element by element, and
 // never stored.
 //
-// A wave owns kRows consecutive output rows.  Per iteration each lane loads 8 consecutive bf16
-// of every row (one 16-byte load per row; the wave covers 512 contiguous elements of each row)
-// and the one sign word holding their bits, widens the weights to fp32, applies +-alpha from
+// A wave owns kRows consecutive output rows.  Per 512-column chunk each lane loads 8 consecutive
+// bf16 of every row (one 16-byte load per row; the wave covers 512 contiguous elements of each
+// row) and the one sign word holding their bits (kU chunks' loads are issued together), widens the weights to fp32, applies +-alpha from
 // the bit by inserting the sign into alpha's bit pattern, and multiply-adds with the lane's 8
 // activations of each token (fp32 accumulation).  Tokens are in segment order, so a token
 // either reuses the previous token's reconstructed value or rebuilds it for its own variant.
@@ -19,6 +19,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = 4;  // output rows per wave
+// 512-column chunks whose loads are in flight together: more for fewer tokens, so the registers
+// of the unrolled loads stay within two waves per SIMD
+template <int M>
+constexpr int chunks_in_flight() { return M == 1 ? 4 : (M == 2 ? 2 : 1); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -74,39 +78,61 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 
   const unsigned pos0 = 8u * (unsigned)(lane & 3);  // bit of the lane's first element in its word
 
-  for (int k0 = lane * 8; k0 < d_in; k0 += 512) {
-    // activations of every token, widened to fp32
-    float xf[M][8];
+  // Each iteration covers kU chunks of 512 columns: every load of the kU chunks is issued before
+  // any is used, so a wave keeps kU * kRows 16-byte weight loads (plus their words and the
+  // activations) in flight.  Columns past d_in read as zero activations and are skipped.
+  constexpr int kU = chunks_in_flight<M>();
+  for (int kb = lane * 8; kb < d_in; kb += 512 * kU) {
+    u32x4 wv[kU][kRows];
+    unsigned word[kU][kRows][M];
+    u32x4 xv[kU][M];
 #pragma unroll
-    for (int t = 0; t < M; ++t) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * d_in + k0);
+    for (int u = 0; u < kU; ++u) {
+      const int k0 = kb + 512 * u;
+      const bool in = k0 < d_in;
+      const int wi = k0 >> 5;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        xf[t][2 * d] = bf16lo_to_f32(xv[d]);
-        xf[t][2 * d + 1] = bf16hi_to_f32(xv[d]);
-      }
-    }
-    const int wi = k0 >> 5;
+      for (int t = 0; t < M; ++t)
+        xv[u][t] = in ? *reinterpret_cast<const u32x4*>(a.x + (size_t)t * d_in + k0)
+                      : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const u32x4 wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + k0));
-      unsigned word[M];
-#pragma unroll
-      for (int t = 0; t < M; ++t) {
-        if (slot[t] >= 0 && fresh[t])
-          word[t] = a.words[slot[t]][sign_quad_offset((a.tiled >> slot[t]) & 1u, rowc[r], wi >> 2,
-                                                      wpr) + (wi & 3)];
-        else
-          word[t] = t > 0 ? word[t - 1] : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wf = (e & 1) ? bf16hi_to_f32(wv[e >> 1]) : bf16lo_to_f32(wv[e >> 1]);
-        float weff = wf;
+      for (int r = 0; r < kRows; ++r) {
+        wv[u][r] = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + k0))
+                      : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int t = 0; t < M; ++t) {
-          if (fresh[t]) weff = slot[t] >= 0 ? wf + signed_alpha(abits[r][t], word[t], pos0 + e) : wf;
-          acc[r][t] = fmaf(weff, xf[t][e], acc[r][t]);
+          if (slot[t] >= 0 && fresh[t])
+            word[u][r][t] = in ? a.words[slot[t]][sign_quad_offset((a.tiled >> slot[t]) & 1u, rowc[r],
+                                                                   wi >> 2, wpr) + (wi & 3)]
+                               : 0u;
+          else
+            word[u][r][t] = t > 0 ? word[u][r][t - 1] : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      // activations of every token, widened to fp32
+      float xf[M][8];
+#pragma unroll
+      for (int t = 0; t < M; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          xf[t][2 * d] = bf16lo_to_f32(xv[u][t][d]);
+          xf[t][2 * d + 1] = bf16hi_to_f32(xv[u][t][d]);
+        }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float wf = (e & 1) ? bf16hi_to_f32(wv[u][r][e >> 1]) : bf16lo_to_f32(wv[u][r][e >> 1]);
+          float weff = wf;
+#pragma unroll
+          for (int t = 0; t < M; ++t) {
+            if (fresh[t])
+              weff = slot[t] >= 0 ? wf + signed_alpha(abits[r][t], word[u][r][t], pos0 + e) : wf;
+            acc[r][t] = fmaf(weff, xf[t][e], acc[r][t]);
+          }
         }
       }
     }
