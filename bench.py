@@ -55,7 +55,7 @@ def parse():
                    help="decode kernel family (auto: what the library picks)")
     p.add_argument("--alpha-rows", action="store_true",
                    help="decode configs: compress every variant with one alpha per output row "
-                        "(the library then runs 5-256 token batches on the streaming kernel)")
+                        "(the split kernel then runs launches of at most 128 tokens)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB device buffer three times (a plain copy kernel of known "
                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -452,8 +452,6 @@ def run_decode(args, torch, bd, config, cpu_baseline=True, rotate=1, unfused=Fal
     achieved = bytes_launch / avg_launch_s / 1e9
     total_elems = sum(L.d_out * L.d_in for blk in step_blocks[0] for L in blk)
     path = bd.auto_path(m, offs, segv) if args.path == "auto" else bd.PATHS[args.path]
-    if args.alpha_rows and path == 4:
-        path = 2  # per-row scales: the library runs the batch on the streaming kernel
     # compress from a weight pair, after the timed region (default workload only)
     pair = measure_compress_pair(torch, bd) if config == 5 else None
     rows = measure_compress_rows(torch, bd) if config == 5 else None
@@ -651,7 +649,13 @@ def sub_results(args, torch, bd, head):
     torch.cuda.empty_cache()
     log("[sub] config 4: prefill, with the unfused comparison")
     out["prefill_4x2048"] = _sub(run_prefill(sub_args, torch, bd, unfused=True))
-    for k in ("gemv_1tok", "block_64tok"):
+    gc.collect()
+    torch.cuda.empty_cache()
+    log("[sub] the headline workload with one alpha per output row")
+    rows_args = argparse.Namespace(**vars(sub_args))
+    rows_args.alpha_rows = True
+    out["alpha_rows_20x70b"] = _sub(run_decode(rows_args, torch, bd, 5, cpu_baseline=False))
+    for k in ("gemv_1tok", "block_64tok", "alpha_rows_20x70b"):
         out[k]["roofline"]["frac_of_copy_ceiling"] = out[k]["roofline"]["achieved"] / ceil["gbs"]
     return out
 

@@ -73,8 +73,9 @@ typedef enum {
   BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
   BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp6 MFMA on a
                               * two-term fp6 split of alpha * x (per-32-column power-of-two
-                              * scales); needs workspace and tiled sign words, and per-matrix
-                              * alpha (AUTO runs a batch with a per-row variant on STREAM)    */
+                              * scales; for a per-row-alpha variant of x, with alpha_r applied
+                              * in fp32, in launches of at most 128 tokens); needs workspace
+                              * and tiled sign words                                         */
 } bitdelta_path;
 
 /* One compressed variant of one weight matrix: the output of bitdelta_compress.  At least one of
@@ -295,7 +296,7 @@ bitdelta_status bitdelta_matmul_grouped(const bitdelta_problem* problems, int32_
  * inputs and outputs as for bitdelta_matmul_grouped.
  *
  *   path  AUTO or SPLIT; a batch the SPLIT path does not serve (AUTO would pick GEMV or PREFILL
- *         for this M, a variant lacks the tiled words or has per-row scales, d_in % 128 != 0)
+ *         for this M, a variant lacks the tiled words, d_in % 128 != 0)
  *         gives UNSUPPORTED: use bitdelta_matmul_grouped for those (they need no workspace).
  * Errors: as bitdelta_matmul_grouped, plus WORKSPACE when the batch needs more than
  * BITDELTA_NOALLOC_SCRATCH_BYTES (the sum over the problems of
@@ -313,8 +314,8 @@ bitdelta_status bitdelta_matmul_grouped_noalloc(const bitdelta_problem* problems
 
 /* The kernel family bitdelta_matmul_grouped's AUTO picks for this batch shape (a bitdelta_path
  * value), or -1 for invalid segments.  Host only.  It sees the shape, not the variants: where it
- * answers SPLIT, a call whose variants lack the tiled sign words or d_in % 128, or that holds a
- * per-row-alpha variant, runs STREAM instead (PREFILL when streaming does not apply either). */
+ * answers SPLIT, a call whose variants lack the tiled sign words or d_in % 128 runs STREAM
+ * instead (PREFILL when streaming does not apply either). */
 int32_t bitdelta_auto_path(int64_t M, const int32_t* seg_offsets, const int32_t* seg_variant,
                            int32_t num_segments);
 

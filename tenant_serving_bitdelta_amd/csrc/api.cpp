@@ -138,7 +138,6 @@ bool split_eligible(const bitdelta_problem* probs, int np, int64_t M, const SegL
       if (s.variant < 0) continue;
       const uint32_t* t = P.variants[s.variant].sign_words_t128;
       if (!t || !aligned(t, 16)) return false;
-      if (P.variants[s.variant].alpha_per_row) return false;  // alpha is folded into x
     }
   }
   return true;
@@ -284,10 +283,11 @@ struct SplitPlan {
 // pair (16 fp4 x fp6 MFMAs and the lane masking) and one expansion of a variant's sign words.
 constexpr int kCostTile = 512, kCostPair = 320, kCostExpand = 224;
 
-bool plan_split(const SegList& segs, int t_begin, int t_end, SplitPlan* pl) {
+// max_tiles: 16, or 8 for launches that may hold per-row-scale variants (one tile per wave).
+bool plan_split(const SegList& segs, int t_begin, int t_end, int max_tiles, SplitPlan* pl) {
   const int tok_base = t_begin / 16 * 16;
   const int ntiles = (t_end - 1 - tok_base) / 16 + 1;
-  if (ntiles > bd::kSplitMaxM / 16) return false;
+  if (ntiles > max_tiles) return false;
   int slot_var[bd::kMaxSlots];
   int nslot = 0;
   int8_t token_slot[bd::kSplitMaxM];
@@ -433,11 +433,19 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, cons
     order[i] = p;
   }
 
+  // A variant with one scale per output row takes its own accumulator set in the kernel, which
+  // fits the registers with one dense tile per wave: launches of such calls cover 128 tokens.
+  bool rows = false;
+  for (int p = 0; p < np; ++p)
+    for (const Segment& sg : segs)
+      if (sg.variant >= 0 && probs[p].variants[sg.variant].alpha_per_row) rows = true;
+  const int max_tiles = rows ? bd::kSplitMaxM / 32 : bd::kSplitMaxM / 16;
+
   int t_begin = 0;
   while (t_begin < M) {
     // grow the launch one run (same variant, same 16-token block) at a time
     SplitPlan plan;
-    const int limit = (int)std::min<int64_t>(M, t_begin / 16 * 16 + bd::kSplitMaxM);
+    const int limit = (int)std::min<int64_t>(M, t_begin / 16 * 16 + 16 * max_tiles);
     int t = t_begin;
     while (t < limit) {
       // the run of token t: same variant (segment), same 16-token block
@@ -446,7 +454,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, cons
         if (sg.begin <= t && t < sg.begin + sg.len) seg_end = sg.begin + sg.len;
       const int e = std::min(std::min(seg_end, limit), (t / 16 + 1) * 16);
       SplitPlan cand;
-      if (!plan_split(segs, t_begin, e, &cand)) break;
+      if (!plan_split(segs, t_begin, e, max_tiles, &cand)) break;
       plan = cand;
       t = e;
     }
@@ -513,9 +521,14 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, cons
         S.d_out = (int)P.d_out;
         S.d_in = (int)P.d_in;
         S.nblocks = (int)((P.d_out + bd::kSplitRows - 1) / bd::kSplitRows);
+        S.alpha_rows = 0;
         for (int s = 0; s < plan.nslot; ++s) {
-          S.words[s] = P.variants[plan.slot_var[s]].sign_words_t128;
-          act.alpha[q][s] = P.variants[plan.slot_var[s]].alpha;
+          const bitdelta_variant& V = P.variants[plan.slot_var[s]];
+          S.words[s] = V.sign_words_t128;
+          // per-matrix alpha scales x in the prologue; per-row alphas are applied by the kernel
+          act.alpha[q][s] = V.alpha_per_row ? nullptr : V.alpha;
+          S.alpha[s] = V.alpha_per_row ? V.alpha : nullptr;
+          if (V.alpha_per_row) S.alpha_rows |= 1u << s;
         }
       }
       bitdelta_status r = map_hip(bd::launch_split_act(act, st));

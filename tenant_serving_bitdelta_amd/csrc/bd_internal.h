@@ -198,8 +198,10 @@ struct SplitProblem {
   const uint16_t* w;
   void* y;                    // [M][d_out] of the whole call
   int d_out, d_in;
-  int nblocks, pad_;          // 128-row blocks of this linear
+  int nblocks;                // 128-row blocks of this linear
+  unsigned alpha_rows;        // bit s set: slot s has one alpha per output row (alpha[s][row])
   const uint32_t* words[kMaxSlots];  // tiled sign words (128-row layout)
+  const float* alpha[kMaxSlots];     // per-row scales of the slots in alpha_rows (else unused)
 };
 
 // Per-wave work of a split launch.  32-bit fields: the kernel reads them with scalar loads
@@ -300,7 +302,8 @@ struct SplitArgs {
   SplitWave wv[8];
   int8_t token_slot[kSplitMaxM];         // slot of token tok_base + t (-1 = base model); read per lane
 };
-// nd: dense tiles per wave (1 or 2); ng: slot groups per wave (at most kSplitMaxGroups).
+// nd: dense tiles per wave (1 or 2); ng: slot groups per wave (at most kSplitMaxGroups).  A launch
+// with per-row slots (any alpha_rows bit) needs nd == 1.
 hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream);
 
 // What the schedule of a split launch depends on: the linears (in launch order) with ns K steps
@@ -322,7 +325,8 @@ struct SplitActArgs {
   unsigned char* xq[kMaxProblems];     // out: fp6 hi/lo terms of alpha * x in sign-operand order
   unsigned char* xs[kMaxProblems];     // out: their block scales
   float* xc[kMaxProblems];             // out: per step and token, the correction sums
-  const float* alpha[kMaxProblems][kMaxSlots];
+  const float* alpha[kMaxProblems][kMaxSlots];  // null: the slot's tokens take x' = x (per-row
+                                               // scales are applied by the main kernel)
   int d_in[kMaxProblems];
   int Mp, tok_base, lo, hi, nprob, pad_;  // tokens [tok_base + lo, tok_base + hi)
   uint64_t* counter;                   // out: ncounter split counters set to zero

@@ -133,9 +133,13 @@ __device__ __forceinline__ void raw_barrier() {
 template <int N>
 constexpr int cmin63() { return N > 63 ? 63 : N; }
 
-template <int ND, int NG>
+// RA: the launch has variants with one scale per output row (ND == 1).  Their pairs accumulate
+// the sign sum of x' = x into a second accumulator set, which each piece scales row by row and
+// adds to the first before its sums leave the registers.
+template <int ND, int NG, bool RA>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, unsigned stage_bytes,
                                                             int nst) {
+  static_assert(!RA || ND == 1, "per-row scales need one dense tile per wave");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // ---- which piece: linear, 128-row block and K steps (wave-uniform) ---------------------------
@@ -232,9 +236,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     coff[i] = tq ? (unsigned)(tb0 + tile) * 256 + (unsigned)lane * 4 : kOob;
   }
   // slot groups: group q holds the pair (dense tile i, variant slot gslot[q][i]) of each tile i
-  // that has one (slot -1: none); pin marks the lanes whose token belongs to that variant
+  // that has one (slot -1: none); pin marks the lanes whose token belongs to that variant; grow
+  // marks groups whose variant has per-row scales (wave-uniform)
   int gslot[NG][ND];
   bool pin[NG][ND];
+  bool grow[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q)
 #pragma unroll
@@ -243,6 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       gslot[q][i] = slot;
       const int t = 16 * a.wv[wave].tile[i] + j;
       pin[q][i] = slot >= 0 && dreal[i] && t >= lo_tok && t < hi_tok && a.token_slot[t] == slot;
+      if (i == 0) grow[q] = RA && slot >= 0 && ((P.alpha_rows >> slot) & 1u);
     }
 
   // ---- registers ------------------------------------------------------------------------------------
@@ -254,6 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   for (int i = 0; i < ND; ++i)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accs[RA ? kRT : 1];  // sign sums of the per-row pairs (tile 0)
+#pragma unroll
+  for (int rt = 0; rt < (RA ? kRT : 1); ++rt) accs[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto load_xb = [&](int i, unsigned s) {
 #pragma unroll
@@ -299,16 +309,23 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   u32x4 S[kRT];
   // Lanes whose token is not of the pair's variant get block scale 2^-127 for both terms, so
   // their products vanish below fp32 resolution (at most 2^-120 in magnitude per product).
-  auto pair_mfma = [&](int i, bool in) {
+  auto pair_mfma = [&](int i, bool in, bool rows) {
     const int sc = in ? (int)xs[i] : 0;
     const i32x8 bh = {(int)xq[i][0][0], (int)xq[i][0][1], (int)xq[i][0][2], (int)xq[i][0][3],
                       (int)xq[i][1][0], (int)xq[i][1][1], 0, 0};
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, sc, acc[i][rt]);
     const i32x8 bl = {(int)xq[i][1][2], (int)xq[i][1][3], (int)xq[i][2][0], (int)xq[i][2][1],
                       (int)xq[i][2][2], (int)xq[i][2][3], 0, 0};
+    if (RA && rows) {
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<1>(S[rt], bl, sc, acc[i][rt]);
+      for (int rt = 0; rt < kRT; ++rt) accs[rt] = mfma_sign<0>(S[rt], bh, sc, accs[rt]);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) accs[rt] = mfma_sign<1>(S[rt], bl, sc, accs[rt]);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, sc, acc[i][rt]);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<1>(S[rt], bl, sc, acc[i][rt]);
+    }
   };
   auto expand = [&](int slot, unsigned st) {
     const unsigned char* sw = smem + st + s_lane + (unsigned)slot * kSSlot;
@@ -328,13 +345,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       const int s0 = gslot[q][0];
       if (s0 >= 0) {
         expand(s0, st);
-        pair_mfma(0, pin[q][0]);
+        pair_mfma(0, pin[q][0], grow[q]);
       }
       if (ND == 2) {
         const int s1 = gslot[q][ND - 1];
         if (s1 >= 0) {
           if (s1 != s0) expand(s1, st);
-          pair_mfma(ND - 1, pin[q][ND - 1]);
+          pair_mfma(ND - 1, pin[q][ND - 1], false);
         }
       }
     }
@@ -399,8 +416,31 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     }
     cs += __shfl_xor(cs, 16);
     cs += __shfl_xor(cs, 32);
+    if (RA) {
+      // a token of a per-row variant: its sign sum is in accs, to be scaled row by row
+      const int ts = tr >= lo_tok && tr < hi_tok ? a.token_slot[tr] : -1;
+      const bool lrow = ts >= 0 && ((P.alpha_rows >> ts) & 1u);
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) acc[i][rt] -= cs;
+      for (int rt = 0; rt < kRT; ++rt) {
+        if (lrow) accs[rt] -= cs;
+        else acc[i][rt] -= cs;
+      }
+      if (lrow) {
+        // acc += alpha_r * (sign sum) for the 4 rows 4g..4g+3 of each row tile the lane holds
+        const float* al = P.alpha[ts];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          const int orow = row0 + rt * 16 + 4 * g;
+          f32x4 av;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[e] = al[min(orow + e, d_out - 1)];
+          acc[i][rt] += av * accs[rt];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) acc[i][rt] -= cs;
+    }
   }
 
   // ---- split unit: leave the sums in this piece's slot; the last piece adds all slots ------------
@@ -591,7 +631,7 @@ __global__ __launch_bounds__(kActThreads) void split_act_kernel(const SplitActAr
 
   // fp6 terms of lane group g: the 32 columns c = g (mod 4) of the step, field f <- column
   // 32 (f / 8) + 4 (f % 8) + g
-  const float alpha = *a.alpha[p][slot];
+  const float alpha = a.alpha[p][slot] ? *a.alpha[p][slot] : 1.0f;  // null: x' = x
   float xp[32];
   float m = 0.f;
 #pragma unroll
@@ -658,15 +698,15 @@ int lds_limit() {
   return v < (int)kLdsCap ? v : (int)kLdsCap;
 }
 
-template <int ND, int NG>
+template <int ND, int NG, bool RA = false>
 hipError_t launch_nd_ng(const SplitArgs& a, int nblocks, unsigned stage, int nst,
                          hipStream_t stream) {
   static DeviceOnce once;
-  hipError_t e = set_dynamic_lds_once(once, reinterpret_cast<const void*>(&split_kernel<ND, NG>),
-                                      lds_limit());
+  hipError_t e = set_dynamic_lds_once(
+      once, reinterpret_cast<const void*>(&split_kernel<ND, NG, RA>), lds_limit());
   if (e != hipSuccess) return e;
   clear_stale_error();
-  hipLaunchKernelGGL((split_kernel<ND, NG>), dim3(nblocks), dim3(kThreads), nst * stage, stream,
+  hipLaunchKernelGGL((split_kernel<ND, NG, RA>), dim3(nblocks), dim3(kThreads), nst * stage, stream,
                      a, stage, nst);
   return hipGetLastError();
 }
@@ -770,6 +810,20 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
   if (nslot > 0 && (!H.partial || !H.counter || !H.stats || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
     return hipErrorInvalidValue;
   const int nblocks = 8 * (nheads + npool);
+  bool rows = false;
+  for (int q = 0; q < a.nprob; ++q) {
+    const SplitProblem& P = a.prob[q];
+    for (int sl = 0; sl < a.nslots; ++sl)
+      if (((P.alpha_rows >> sl) & 1u) && !P.alpha[sl]) return hipErrorInvalidValue;
+    rows = rows || (P.alpha_rows & ((1u << a.nslots) - 1u)) != 0u;
+  }
+  if (rows) {
+    if (nd != 1) return hipErrorInvalidValue;
+    if (ng <= 1) return launch_nd_ng<1, 1, true>(a, nblocks, stage, nst, stream);
+    if (ng <= 2) return launch_nd_ng<1, 2, true>(a, nblocks, stage, nst, stream);
+    if (ng <= 4) return launch_nd_ng<1, 4, true>(a, nblocks, stage, nst, stream);
+    return launch_nd_ng<1, 8, true>(a, nblocks, stage, nst, stream);
+  }
   if (nd == 1) {
     if (ng <= 1) return launch_nd_ng<1, 1>(a, nblocks, stage, nst, stream);
     if (ng <= 2) return launch_nd_ng<1, 2>(a, nblocks, stage, nst, stream);

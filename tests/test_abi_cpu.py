@@ -145,8 +145,7 @@ def test_compress_rows_validation():
 
 
 def test_alpha_per_row_flag_validation():
-    """alpha_per_row must be 0 or 1; a forced split launch refuses per-row variants (it folds the
-    scale into the activations), before anything is enqueued."""
+    """alpha_per_row must be 0 or 1, checked before anything is enqueued."""
     o = np.array([0, 8], dtype=np.int32)
     v = np.array([0], dtype=np.int32)
     op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -158,7 +157,7 @@ def test_alpha_per_row_flag_validation():
     prob[0].d_out, prob[0].d_in = 256, 256
     prob[0].variants = ctypes.cast(varr, ctypes.POINTER(bd._Variant))
     prob[0].num_variants = 1
-    for flag, path, want in [(2, 0, INVALID), (-1, 0, INVALID), (1, 4, UNSUPPORTED)]:
+    for flag, path, want in [(2, 0, INVALID), (-1, 0, INVALID)]:
         varr[0].alpha_per_row = flag
         assert L.bitdelta_matmul_grouped(prob, 1, 8, op, vp, 1, 0, path, FAKE, 1 << 40, None) == want
 
