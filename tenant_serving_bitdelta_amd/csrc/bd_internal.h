@@ -155,7 +155,8 @@ struct StreamArgs {
 hipError_t launch_stream(const StreamArgs& a, int nblocks, hipStream_t stream);
 size_t stream_lds_bytes(int ntiles, int nslots);
 
-// Prefill: per-segment tiles of 256 tokens x 256 output rows, W_eff rebuilt in LDS.
+// Prefill: per-segment tiles of 256 tokens x 256 output rows, W_eff rebuilt in registers from
+// raw weights staged in LDS.
 constexpr int kPrefillBM = 256;
 constexpr int kPrefillBN = 256;
 constexpr int kPrefillMaxMTiles = 256;
@@ -165,9 +166,10 @@ struct PrefillArgs {
   const uint16_t* w;
   void* y;
   int d_out, d_in, y_f32, n_mtiles, n_ntiles;
-  int vec_signs;                       // bit s set: slot s's words are read 16 bytes (4 steps)
+  int vec_signs;                       // bit s set: slot s's words may be read 16 bytes (4 steps)
                                        // at a time (d_in % 128 == 0 and tiled or 16-byte aligned
-                                       // row-major words); bit 31: base-model tiles
+                                       // row-major words); bit 31: base-model tiles.  The kernel
+                                       // reads quads when every bit is set, else single words
   unsigned alpha_rows;                 // bit s set: slot s has one alpha per output row
   unsigned tiled;                      // bit s set: slot s's words are in the 128-row tiled
                                        // layout (then its vec_signs bit is set)
