@@ -54,8 +54,7 @@ def parse():
     p.add_argument("--path", default="auto", choices=("auto", "gemv", "stream", "split", "prefill"),
                    help="decode kernel family (auto: what the library picks)")
     p.add_argument("--alpha-rows", action="store_true",
-                   help="decode configs: compress every variant with one alpha per output row "
-                        "(the split kernel then runs launches of at most 128 tokens)")
+                   help="decode configs: compress every variant with one alpha per output row")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB device buffer three times (a plain copy kernel of known "
                         "size, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")

@@ -70,12 +70,12 @@ typedef enum {
   BITDELTA_PATH_GEMV = 1,    /* fp32 reconstruction in registers, VALU; M <= 4                 */
   BITDELTA_PATH_STREAM = 2,  /* decode: base and sign sums both as bf16 MFMA; no workspace;
                               * d_in % 128 == 0                                               */
-  BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff tile rebuilt in LDS    */
+  BITDELTA_PATH_PREFILL = 3, /* prefill: per-segment tiles, bf16 W_eff rebuilt in registers   */
   BITDELTA_PATH_SPLIT = 4    /* decode: base sum bf16 MFMA, sign sum fp4 x fp6 MFMA on a
                               * two-term fp6 split of alpha * x (per-32-column power-of-two
-                              * scales; for a per-row-alpha variant of x, with alpha_r applied
-                              * in fp32, in launches of at most 128 tokens); needs workspace
-                              * and tiled sign words                                         */
+                              * scales; for a per-row-alpha variant of x, with each step's
+                              * sums times alpha_r in fp32); needs workspace and tiled sign
+                              * words                                                        */
 } bitdelta_path;
 
 /* One compressed variant of one weight matrix: the output of bitdelta_compress.  At least one of

@@ -283,7 +283,7 @@ struct SplitPlan {
 // pair (16 fp4 x fp6 MFMAs and the lane masking) and one expansion of a variant's sign words.
 constexpr int kCostTile = 512, kCostPair = 320, kCostExpand = 224;
 
-// max_tiles: 16, or 8 for launches that may hold per-row-scale variants (one tile per wave).
+// max_tiles: dense 16-token tiles one launch may hold (16).
 bool plan_split(const SegList& segs, int t_begin, int t_end, int max_tiles, SplitPlan* pl) {
   const int tok_base = t_begin / 16 * 16;
   const int ntiles = (t_end - 1 - tok_base) / 16 + 1;
@@ -433,13 +433,7 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, cons
     order[i] = p;
   }
 
-  // A variant with one scale per output row takes its own accumulator set in the kernel, which
-  // fits the registers with one dense tile per wave: launches of such calls cover 128 tokens.
-  bool rows = false;
-  for (int p = 0; p < np; ++p)
-    for (const Segment& sg : segs)
-      if (sg.variant >= 0 && probs[p].variants[sg.variant].alpha_per_row) rows = true;
-  const int max_tiles = rows ? bd::kSplitMaxM / 32 : bd::kSplitMaxM / 16;
+  const int max_tiles = bd::kSplitMaxM / 16;
 
   int t_begin = 0;
   while (t_begin < M) {

@@ -67,7 +67,9 @@ constexpr unsigned kWStage = kRows * kKS * 2;        // 32 KiB of W_base per ste
 constexpr unsigned kSSlot = kRows * 16;              // one variant's sign words, one step: 2 KiB
 constexpr unsigned kLdsCap = 160 * 1024;             // LDS of one compute unit
 constexpr int kCopyWaves = 4;                        // waves that issue the global->LDS copies
-static_assert(kWStage + kMaxSlots * kSSlot <= kLdsCap / 2, "two stages must fit in LDS");
+constexpr unsigned kRowScaleBytes = kMaxSlots * kRows * 4;  // per-row scales of a block, fp32
+static_assert(kWStage + kMaxSlots * kSSlot <= (kLdsCap - kRowScaleBytes) / 2,
+              "two stages and the row scales must fit in LDS");
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -133,13 +135,17 @@ __device__ __forceinline__ void raw_barrier() {
 template <int N>
 constexpr int cmin63() { return N > 63 ? 63 : N; }
 
-// RA: the launch has variants with one scale per output row (ND == 1).  Their pairs accumulate
-// the sign sum of x' = x into a second accumulator set, which each piece scales row by row and
-// adds to the first before its sums leave the registers.
-template <int ND, int NG, bool RA>
+// RA: the launch has variants with one scale per output row; their pairs multiply x' = x (the
+// prologue leaves it unscaled).  kRowsAcc (one dense tile per wave): the pairs sum into a second
+// accumulator set, which each piece scales row by row and adds to the first before its sums
+// leave the registers.  kRowsStep (two tiles per wave, where a second set does not fit the
+// registers): each step's sign sums of a pair are added to the accumulators scaled row by row in
+// fp32 (the scales of the block's 128 rows wait in LDS past the copy ring, kRowScaleBytes).
+constexpr int kRowsNone = 0, kRowsAcc = 1, kRowsStep = 2;
+template <int ND, int NG, int RA>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, unsigned stage_bytes,
                                                             int nst) {
-  static_assert(!RA || ND == 1, "per-row scales need one dense tile per wave");
+  static_assert(RA != kRowsAcc || ND == 1, "a second accumulator set fits one dense tile");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   // ---- which piece: linear, 128-row block and K steps (wave-uniform) ---------------------------
@@ -237,10 +243,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   }
   // slot groups: group q holds the pair (dense tile i, variant slot gslot[q][i]) of each tile i
   // that has one (slot -1: none); pin marks the lanes whose token belongs to that variant; grow
-  // marks groups whose variant has per-row scales (wave-uniform)
+  // marks the pairs whose variant has per-row scales (wave-uniform)
   int gslot[NG][ND];
   bool pin[NG][ND];
-  bool grow[NG];
+  bool grow[NG][ND];
 #pragma unroll
   for (int q = 0; q < NG; ++q)
 #pragma unroll
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       gslot[q][i] = slot;
       const int t = 16 * a.wv[wave].tile[i] + j;
       pin[q][i] = slot >= 0 && dreal[i] && t >= lo_tok && t < hi_tok && a.token_slot[t] == slot;
-      if (i == 0) grow[q] = RA && slot >= 0 && ((P.alpha_rows >> slot) & 1u);
+      grow[q][i] = RA != kRowsNone && slot >= 0 && ((P.alpha_rows >> slot) & 1u);
     }
 
   // ---- registers ------------------------------------------------------------------------------------
@@ -261,9 +267,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   for (int i = 0; i < ND; ++i)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 accs[RA ? kRT : 1];  // sign sums of the per-row pairs (tile 0)
+  f32x4 accs[RA == kRowsAcc ? kRT : 1];  // kRowsAcc: sign sums of the per-row pairs (tile 0)
 #pragma unroll
-  for (int rt = 0; rt < (RA ? kRT : 1); ++rt) accs[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < (RA == kRowsAcc ? kRT : 1); ++rt) accs[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // kRowsStep: slot sl's scales of rows row0 .. row0 + 127 at float 128 sl (rows past d_out
+  // repeat the last row's)
+  float* const rscale = reinterpret_cast<float*>(smem + (unsigned)nst * stage_bytes);
+  if (RA == kRowsStep) {
+    for (int e = tid; e < nslots * kRows; e += kThreads) {
+      const int sl = e / kRows, r = e - sl * kRows;
+      if ((P.alpha_rows >> sl) & 1u) rscale[e] = P.alpha[sl][min(row0 + r, d_out - 1)];
+    }
+  }
 
   auto load_xb = [&](int i, unsigned s) {
 #pragma unroll
@@ -289,6 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   for (int i = 0; i < ND; ++i) load_xb(i, (unsigned)k0);
   __builtin_amdgcn_sched_barrier(0);
   SPLIT_VMCNT(cmin63<kX>());
+  if (RA == kRowsStep) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): scale stores in LDS
   raw_barrier();
 
   // per-lane LDS read offsets
@@ -309,17 +325,32 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   u32x4 S[kRT];
   // Lanes whose token is not of the pair's variant get block scale 2^-127 for both terms, so
   // their products vanish below fp32 resolution (at most 2^-120 in magnitude per product).
-  auto pair_mfma = [&](int i, bool in, bool rows) {
+  // A per-row pair (rows, variant slot sl) sums 4 row tiles at a time from zero and adds the sums
+  // times the rows' scales (lane: rows 4g .. 4g + 3 of each row tile).
+  auto pair_mfma = [&](int i, bool in, bool rows, int sl) {
     const int sc = in ? (int)xs[i] : 0;
     const i32x8 bh = {(int)xq[i][0][0], (int)xq[i][0][1], (int)xq[i][0][2], (int)xq[i][0][3],
                       (int)xq[i][1][0], (int)xq[i][1][1], 0, 0};
     const i32x8 bl = {(int)xq[i][1][2], (int)xq[i][1][3], (int)xq[i][2][0], (int)xq[i][2][1],
                       (int)xq[i][2][2], (int)xq[i][2][3], 0, 0};
-    if (RA && rows) {
+    if (RA == kRowsAcc && rows) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) accs[rt] = mfma_sign<0>(S[rt], bh, sc, accs[rt]);
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) accs[rt] = mfma_sign<1>(S[rt], bl, sc, accs[rt]);
+    } else if (RA == kRowsStep && rows) {
+      const float* rs = rscale + sl * kRows + 4 * g;
+#pragma unroll
+      for (int r0 = 0; r0 < kRT; r0 += 4) {
+        f32x4 t[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t[u] = mfma_sign<0>(S[r0 + u], bh, sc, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t[u] = mfma_sign<1>(S[r0 + u], bl, sc, t[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[i][r0 + u] += *reinterpret_cast<const f32x4*>(rs + 16 * (r0 + u)) * t[u];
+      }
     } else {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, sc, acc[i][rt]);
@@ -345,13 +376,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       const int s0 = gslot[q][0];
       if (s0 >= 0) {
         expand(s0, st);
-        pair_mfma(0, pin[q][0], grow[q]);
+        pair_mfma(0, pin[q][0], grow[q][0], s0);
       }
       if (ND == 2) {
         const int s1 = gslot[q][ND - 1];
         if (s1 >= 0) {
           if (s1 != s0) expand(s1, st);
-          pair_mfma(ND - 1, pin[q][ND - 1], false);
+          pair_mfma(ND - 1, pin[q][ND - 1], grow[q][ND - 1], s1);
         }
       }
     }
@@ -416,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     }
     cs += __shfl_xor(cs, 16);
     cs += __shfl_xor(cs, 32);
-    if (RA) {
+    if (RA == kRowsAcc) {
       // a token of a per-row variant: its sign sum is in accs, to be scaled row by row
       const int ts = tr >= lo_tok && tr < hi_tok ? a.token_slot[tr] : -1;
       const bool lrow = ts >= 0 && ((P.alpha_rows >> ts) & 1u);
@@ -436,6 +467,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
           for (int e = 0; e < 4; ++e) av[e] = al[min(orow + e, d_out - 1)];
           acc[i][rt] += av * accs[rt];
         }
+      }
+    } else if (RA == kRowsStep) {
+      // a token of a per-row variant: its sign sums were added times alpha_r, and so is the
+      // correction (the lane's rows 4g..4g+3 of each row tile)
+      const int ts = tr >= lo_tok && tr < hi_tok ? a.token_slot[tr] : -1;
+      const bool lrow = ts >= 0 && ((P.alpha_rows >> ts) & 1u);
+      const float* rs = rscale + (lrow ? ts : 0) * kRows + 4 * g;
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        if (lrow) acc[i][rt] -= *reinterpret_cast<const f32x4*>(rs + 16 * rt) * cs;
+        else acc[i][rt] -= cs;
       }
     } else {
 #pragma unroll
@@ -698,7 +740,7 @@ int lds_limit() {
   return v < (int)kLdsCap ? v : (int)kLdsCap;
 }
 
-template <int ND, int NG, bool RA = false>
+template <int ND, int NG, int RA = kRowsNone>
 hipError_t launch_nd_ng(const SplitArgs& a, int nblocks, unsigned stage, int nst,
                          hipStream_t stream) {
   static DeviceOnce once;
@@ -706,8 +748,8 @@ hipError_t launch_nd_ng(const SplitArgs& a, int nblocks, unsigned stage, int nst
       once, reinterpret_cast<const void*>(&split_kernel<ND, NG, RA>), lds_limit());
   if (e != hipSuccess) return e;
   clear_stale_error();
-  hipLaunchKernelGGL((split_kernel<ND, NG, RA>), dim3(nblocks), dim3(kThreads), nst * stage, stream,
-                     a, stage, nst);
+  hipLaunchKernelGGL((split_kernel<ND, NG, RA>), dim3(nblocks), dim3(kThreads),
+                     nst * stage + (RA == kRowsStep ? kRowScaleBytes : 0u), stream, a, stage, nst);
   return hipGetLastError();
 }
 
@@ -777,7 +819,16 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
       }
   }
   if (copy_shares != (1u << kCopyWaves) - 1u) return hipErrorInvalidValue;  // every copy issued
-  const int lds = lds_limit();
+  // variants with one scale per output row: with two tiles per wave their scales take
+  // kRowScaleBytes of LDS past the ring
+  bool rows = false;
+  for (int q = 0; q < a.nprob; ++q) {
+    const SplitProblem& P = a.prob[q];
+    for (int sl = 0; sl < a.nslots; ++sl)
+      if (((P.alpha_rows >> sl) & 1u) && !P.alpha[sl]) return hipErrorInvalidValue;
+    rows = rows || (P.alpha_rows & ((1u << a.nslots) - 1u)) != 0u;
+  }
+  const int lds = lds_limit() - (rows && nd == 2 ? (int)kRowScaleBytes : 0);
   const unsigned stage = kWStage + (unsigned)a.nslots * kSSlot;
   int nst = lds / (int)stage;
   nst = nst > 4 ? 4 : nst;
@@ -810,19 +861,17 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
   if (nslot > 0 && (!H.partial || !H.counter || !H.stats || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
     return hipErrorInvalidValue;
   const int nblocks = 8 * (nheads + npool);
-  bool rows = false;
-  for (int q = 0; q < a.nprob; ++q) {
-    const SplitProblem& P = a.prob[q];
-    for (int sl = 0; sl < a.nslots; ++sl)
-      if (((P.alpha_rows >> sl) & 1u) && !P.alpha[sl]) return hipErrorInvalidValue;
-    rows = rows || (P.alpha_rows & ((1u << a.nslots) - 1u)) != 0u;
-  }
   if (rows) {
-    if (nd != 1) return hipErrorInvalidValue;
-    if (ng <= 1) return launch_nd_ng<1, 1, true>(a, nblocks, stage, nst, stream);
-    if (ng <= 2) return launch_nd_ng<1, 2, true>(a, nblocks, stage, nst, stream);
-    if (ng <= 4) return launch_nd_ng<1, 4, true>(a, nblocks, stage, nst, stream);
-    return launch_nd_ng<1, 8, true>(a, nblocks, stage, nst, stream);
+    if (nd == 1) {
+      if (ng <= 1) return launch_nd_ng<1, 1, kRowsAcc>(a, nblocks, stage, nst, stream);
+      if (ng <= 2) return launch_nd_ng<1, 2, kRowsAcc>(a, nblocks, stage, nst, stream);
+      if (ng <= 4) return launch_nd_ng<1, 4, kRowsAcc>(a, nblocks, stage, nst, stream);
+      return launch_nd_ng<1, 8, kRowsAcc>(a, nblocks, stage, nst, stream);
+    }
+    if (ng <= 1) return launch_nd_ng<2, 1, kRowsStep>(a, nblocks, stage, nst, stream);
+    if (ng <= 2) return launch_nd_ng<2, 2, kRowsStep>(a, nblocks, stage, nst, stream);
+    if (ng <= 4) return launch_nd_ng<2, 4, kRowsStep>(a, nblocks, stage, nst, stream);
+    return launch_nd_ng<2, 8, kRowsStep>(a, nblocks, stage, nst, stream);
   }
   if (nd == 1) {
     if (ng <= 1) return launch_nd_ng<1, 1>(a, nblocks, stage, nst, stream);
