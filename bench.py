@@ -44,10 +44,12 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=None, choices=(2, 3, 4, 5),
                    help="run one workload alone (default: the headline plus every sub-result)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the HIP-graph replay timing of the decode block / step workloads")
     p.add_argument("--no-sub", action="store_true", help="default run: the headline only")
     p.add_argument("--unfused", action="store_true",
                    help="--config 3 or 4: also time the unfused comparison")
@@ -186,9 +188,61 @@ class EventTimer:
         self.pairs.append((self._open, e))
         self.bytes += nbytes
 
-    def total_ms(self):
+    def durations_ms(self):
         self.torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in self.pairs)
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+    def total_ms(self):
+        return sum(self.durations_ms())
+
+
+def spread(values, scale=1.0):
+    """Median, p10 and p90 of ``values`` (times ``scale``)."""
+    v = np.asarray(values, dtype=np.float64) * scale
+    if v.size == 0:
+        return None
+    return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+            "p90": float(np.percentile(v, 90)), "n": int(v.size)}
+
+
+def measure_graph_step(args, torch, run_step, outputs, tokens, checks=3):
+    """One whole step (every grouped call of it) captured once into a HIP graph and replayed.
+    Each of ``checks`` replays is compared bit for bit with an eager step, with the outputs
+    cleared and the eager step run between replays; then ``args.steps`` replays are timed, each
+    between HIP events, and their wall time over the lot gives tokens/s."""
+    run_step()
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_step()
+    torch.cuda.synchronize()
+    equal = True
+    for _ in range(checks):
+        for y in outputs:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        equal = equal and all(torch.equal(y, r) for y, r in zip(outputs, ref))
+        run_step()
+        torch.cuda.synchronize()
+        equal = equal and all(torch.equal(y, r) for y, r in zip(outputs, ref))
+    for _ in range(args.warmup):
+        g.replay()
+    rt = EventTimer(torch, reserve=args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rt.start()
+        g.replay()
+        rt.stop()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    del g
+    return {"tokens_per_s": tokens * 1e3 / ms, "ms_per_step": ms,
+            "replay_ms": spread(rt.durations_ms()),
+            "replays_checked": checks, "equal_to_eager": bool(equal)}
 
 
 def measure_compress_pair(torch, bd, reps=5):
@@ -445,30 +499,43 @@ def run_decode(args, torch, bd, config, cpu_baseline=True, rotate=1, unfused=Fal
     step_blocks = [layers] if rotate == 1 else [[blk] for blk in layers]
     step_no = [0]
 
-    def step(timer=None):
+    def run_blocks(blocks_of_step, timer=None):
         # plan (host) + one grouped call per block (split path: activation prologue + main kernel)
         _, o, s = bd.plan_segments(ids, nvar)
-        for blk in step_blocks[step_no[0] % len(step_blocks)]:
+        for blk in blocks_of_step:
             probs = [(L.x, L.w, L.y, L.variants) for L in blk]
             if timer:
                 timer.start()
             bd.matmul_grouped(probs, o, s, path=args.path, workspace=ws)
             if timer:
                 timer.stop()
+
+    def step(timer=None, step_timer=None):
+        if step_timer:
+            step_timer.start()
+        run_blocks(step_blocks[step_no[0] % len(step_blocks)], timer)
+        if step_timer:
+            step_timer.stop()
         step_no[0] += 1
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     kt = EventTimer(torch, reserve=args.steps * len(layers))
+    st = EventTimer(torch, reserve=args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(kt)
+        step(kt, st)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = kt.total_ms()
+    launch_ms = kt.durations_ms()
+    kern_ms = sum(launch_ms)
+    step_ms = st.durations_ms()
+    graph = (measure_graph_step(args, torch, lambda: run_blocks(step_blocks[0]),
+                                [L.y for blk in step_blocks[0] for L in blk], m)
+             if config in (3, 5) and not args.no_graph else None)
     launches = len(kt.pairs)
     bytes_launch = decode_bytes(layers[0], m, n_active, args.alpha_rows)  # every block has the same shapes
     avg_launch_s = kern_ms / launches / 1e3
@@ -517,7 +584,10 @@ def run_decode(args, torch, bd, config, cpu_baseline=True, rotate=1, unfused=Fal
                      "traffic": measured_traffic() if (config == 5 and path == 4) else None,
                      "kernel": {1: "gemv_kernel", 2: "stream_kernel",
                                 4: "split_act_kernel + split_kernel"}.get(path, "?"),
-                     "bytes_per_launch": bytes_launch, "avg_launch_us": avg_launch_s * 1e6},
+                     "bytes_per_launch": bytes_launch, "avg_launch_us": avg_launch_s * 1e6,
+                     "launch_us": spread(launch_ms, 1e3)},
+        "step_ms": spread(step_ms),
+        "graph": graph,
         "compress": {"matrices": len(comp.pairs), "bytes": comp_bytes, "ms": comp_ms,
                      "gbs": comp_bytes / (comp_ms / 1e3) / 1e9,
                      "frac": comp_bytes / (comp_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
@@ -564,7 +634,8 @@ def run_prefill(args, torch, bd, unfused=False):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = kt.total_ms() / len(kt.pairs)
+    launch_ms = kt.durations_ms()
+    kern_ms = sum(launch_ms) / len(launch_ms)
     flops = sum(2.0 * m * L.d_out * L.d_in for L in layers)
     achieved = flops / (kern_ms / 1e3) / 1e12
     unf = None
@@ -583,7 +654,7 @@ def run_prefill(args, torch, bd, unfused=False):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "prefill_kernel", "flops_per_launch": flops,
-                     "avg_launch_us": kern_ms * 1e3},
+                     "avg_launch_us": kern_ms * 1e3, "launch_us": spread(launch_ms, 1e3)},
         "unfused": unf,
         "cpu_baseline": None,
     }
@@ -619,12 +690,13 @@ def main():
 
 def _sub(r):
     """The fields of a workload's result that the headline line carries for it."""
-    keep = ("value", "unit", "ms_per_step", "dtype", "unfused")
+    keep = ("value", "unit", "ms_per_step", "dtype", "unfused", "step_ms", "graph")
     d = {k: r[k] for k in keep if k in r}
     d["workload"] = r["config"]["workload"]
     d["config_index"] = r["config"]["config_index"]
     d["roofline"] = {k: r["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac",
-                                                   "kernel", "avg_launch_us") if k in r["roofline"]}
+                                                   "kernel", "avg_launch_us", "launch_us")
+                      if k in r["roofline"]}
     return d
 
 
