@@ -67,7 +67,10 @@ constexpr unsigned kWStage = kRows * kKS * 2;        // 32 KiB of W_base per ste
 constexpr unsigned kSSlot = kRows * 16;              // one variant's sign words, one step: 2 KiB
 constexpr unsigned kLdsCap = 160 * 1024;             // LDS of one compute unit
 constexpr int kCopyWaves = 4;                        // waves that issue the global->LDS copies
-constexpr unsigned kRowScaleBytes = kMaxSlots * kRows * 4;  // per-row scales of a block, fp32
+// per-row scales of a block, fp32, one run of kRows + 4 floats per variant slot (the padding
+// puts the runs of different slots on different LDS banks)
+constexpr int kRScaleStride = kRows + 4;
+constexpr unsigned kRowScaleBytes = kMaxSlots * kRScaleStride * 4;
 static_assert(kWStage + kMaxSlots * kSSlot <= (kLdsCap - kRowScaleBytes) / 2,
               "two stages and the row scales must fit in LDS");
 
@@ -139,8 +142,10 @@ constexpr int cmin63() { return N > 63 ? 63 : N; }
 // prologue leaves it unscaled).  kRowsAcc (one dense tile per wave): the pairs sum into a second
 // accumulator set, which each piece scales row by row and adds to the first before its sums
 // leave the registers.  kRowsStep (two tiles per wave, where a second set does not fit the
-// registers): each step's sign sums of a pair are added to the accumulators scaled row by row in
-// fp32 (the scales of the block's 128 rows wait in LDS past the copy ring, kRowScaleBytes).
+// registers): each step, every pair of a dense tile sums into one temporary set, which is added
+// to the accumulators times the scale of each lane's token and row (1 for a variant with one
+// scale per matrix, whose activations already carry it); the scales of the block's 128 rows wait
+// in LDS past the copy ring (kRowScaleBytes).
 constexpr int kRowsNone = 0, kRowsAcc = 1, kRowsStep = 2;
 template <int ND, int NG, int RA>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, unsigned stage_bytes,
@@ -270,13 +275,22 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   f32x4 accs[RA == kRowsAcc ? kRT : 1];  // kRowsAcc: sign sums of the per-row pairs (tile 0)
 #pragma unroll
   for (int rt = 0; rt < (RA == kRowsAcc ? kRT : 1); ++rt) accs[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // kRowsStep: slot sl's scales of rows row0 .. row0 + 127 at float 128 sl (rows past d_out
-  // repeat the last row's)
+  // kRowsStep: slot sl's scales of rows row0 .. row0 + 127 at float kRScaleStride * sl (rows
+  // past d_out repeat the last row's; 1 for a slot with one scale per matrix), and each lane's
+  // offset there for its token in dense tile i (slot 0 for lanes without a token)
   float* const rscale = reinterpret_cast<float*>(smem + (unsigned)nst * stage_bytes);
+  unsigned rsl[ND];
   if (RA == kRowsStep) {
     for (int e = tid; e < nslots * kRows; e += kThreads) {
       const int sl = e / kRows, r = e - sl * kRows;
-      if ((P.alpha_rows >> sl) & 1u) rscale[e] = P.alpha[sl][min(row0 + r, d_out - 1)];
+      rscale[sl * kRScaleStride + r] =
+          ((P.alpha_rows >> sl) & 1u) ? P.alpha[sl][min(row0 + r, d_out - 1)] : 1.f;
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int t = 16 * a.wv[wave].tile[i] + j;
+      const int ts = dreal[i] && t >= lo_tok && t < hi_tok ? a.token_slot[t] : -1;
+      rsl[i] = (unsigned)(ts >= 0 ? ts : 0) * kRScaleStride + 4 * g;
     }
   }
 
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   // their products vanish below fp32 resolution (at most 2^-120 in magnitude per product).
   // A per-row pair (rows, variant slot sl) sums 4 row tiles at a time from zero and adds the sums
   // times the rows' scales (lane: rows 4g .. 4g + 3 of each row tile).
-  auto pair_mfma = [&](int i, bool in, bool rows, int sl) {
+  auto pair_mfma = [&](int i, bool in, bool rows) {
     const int sc = in ? (int)xs[i] : 0;
     const i32x8 bh = {(int)xq[i][0][0], (int)xq[i][0][1], (int)xq[i][0][2], (int)xq[i][0][3],
                       (int)xq[i][1][0], (int)xq[i][1][1], 0, 0};
@@ -338,19 +352,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       for (int rt = 0; rt < kRT; ++rt) accs[rt] = mfma_sign<0>(S[rt], bh, sc, accs[rt]);
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) accs[rt] = mfma_sign<1>(S[rt], bl, sc, accs[rt]);
-    } else if (RA == kRowsStep && rows) {
-      const float* rs = rscale + sl * kRows + 4 * g;
-#pragma unroll
-      for (int r0 = 0; r0 < kRT; r0 += 4) {
-        f32x4 t[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) t[u] = mfma_sign<0>(S[r0 + u], bh, sc, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int u = 0; u < 4; ++u) t[u] = mfma_sign<1>(S[r0 + u], bl, sc, t[u]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[i][r0 + u] += *reinterpret_cast<const f32x4*>(rs + 16 * (r0 + u)) * t[u];
-      }
     } else {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma_sign<0>(S[rt], bh, sc, acc[i][rt]);
@@ -366,7 +367,54 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       S[rt] = u32x4{(w[0] & sm1) ^ sm2, (w[1] & sm1) ^ sm2, (w[2] & sm1) ^ sm2, (w[3] & sm1) ^ sm2};
     }
   };
+  // kRowsStep: the sign sums of pair (dense tile i, the expanded variant) into t
+  auto pair_into = [&](f32x4(&t)[kRT], int i, bool in) {
+    const int sc = in ? (int)xs[i] : 0;
+    const i32x8 bh = {(int)xq[i][0][0], (int)xq[i][0][1], (int)xq[i][0][2], (int)xq[i][0][3],
+                      (int)xq[i][1][0], (int)xq[i][1][1], 0, 0};
+    const i32x8 bl = {(int)xq[i][1][2], (int)xq[i][1][3], (int)xq[i][2][0], (int)xq[i][2][1],
+                      (int)xq[i][2][2], (int)xq[i][2][3], 0, 0};
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) t[rt] = mfma_sign<0>(S[rt], bh, sc, t[rt]);
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) t[rt] = mfma_sign<1>(S[rt], bl, sc, t[rt]);
+  };
   auto sign_phase = [&](bool copies, int cs, unsigned cst, unsigned st) {
+    if (RA == kRowsStep) {
+      // tile by tile: tile 0 takes its groups last to first and tile 1 first to last, so a
+      // variant of both tiles (the first groups) is expanded once when it is the only one
+      int cur = -1;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        f32x4 t[kRT];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) t[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int qq = 0; qq < NG; ++qq) {
+          if (copies) {
+            constexpr int kPer = 16 / (ND * NG);
+            const int it = i * NG + qq;
+#pragma unroll
+            for (int k = it * kPer; k < (it + 1) * kPer; ++k) copy(k, cs, cst);
+          }
+          const int q = i == 0 ? NG - 1 - qq : qq;
+          const int sl = gslot[q][i];
+          if (sl >= 0) {
+            if (sl != cur) {
+              expand(sl, st);
+              cur = sl;
+            }
+            pair_into(t, i, pin[q][i]);
+          }
+        }
+        if (dreal[i]) {
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+            acc[i][rt] += *reinterpret_cast<const f32x4*>(rscale + rsl[i] + 16 * rt) * t[rt];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       if (copies) {
@@ -376,13 +424,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       const int s0 = gslot[q][0];
       if (s0 >= 0) {
         expand(s0, st);
-        pair_mfma(0, pin[q][0], grow[q][0], s0);
+        pair_mfma(0, pin[q][0], grow[q][0]);
       }
       if (ND == 2) {
         const int s1 = gslot[q][ND - 1];
         if (s1 >= 0) {
           if (s1 != s0) expand(s1, st);
-          pair_mfma(ND - 1, pin[q][ND - 1], grow[q][ND - 1], s1);
+          pair_mfma(ND - 1, pin[q][ND - 1], grow[q][ND - 1]);
         }
       }
     }
@@ -473,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       // correction (the lane's rows 4g..4g+3 of each row tile)
       const int ts = tr >= lo_tok && tr < hi_tok ? a.token_slot[tr] : -1;
       const bool lrow = ts >= 0 && ((P.alpha_rows >> ts) & 1u);
-      const float* rs = rscale + (lrow ? ts : 0) * kRows + 4 * g;
+      const float* rs = rscale + (lrow ? ts : 0) * kRScaleStride + 4 * g;
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         if (lrow) acc[i][rt] -= *reinterpret_cast<const f32x4*>(rs + 16 * rt) * cs;
