@@ -270,8 +270,9 @@ bitdelta_status run_stream(const bitdelta_problem* probs, int np, const SegList&
 // a wave share one expansion of the sign words; a wave's pairs are arranged as slot groups, one
 // variant per group.  Tile units go to the waves longest first, each to the SIMD (waves w and
 // w + 4) with the least estimated work.  A launch ends before the first run of same-variant
-// tokens that would give a wave more than kSplitMaxGroups groups.  The less loaded wave of each
-// SIMD issues that SIMD's share of the global->LDS copies.
+// tokens that would give a wave more than kSplitMaxGroups groups.  With two tiles per wave every
+// wave issues one share of the global->LDS copies; with one, the less loaded wave of each SIMD
+// issues that SIMD's share.
 struct SplitPlan {
   int t_begin = 0, t_end = 0, tok_base = 0, nd = 1, ng = 0, nslot = 0;
   int slot_var[bd::kMaxSlots];
@@ -351,8 +352,6 @@ bool plan_split(const SegList& segs, int t_begin, int t_end, int max_tiles, Spli
     wave_of[k] = best + 4 * simd_waves[best]++;
     simd_load[best] += units[k].cost;
   }
-  int wave_load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int k = 0; k < nunits; ++k) wave_load[wave_of[k]] = units[k].cost;
   pl->t_begin = t_begin;
   pl->t_end = t_end;
   pl->tok_base = tok_base;
@@ -365,12 +364,16 @@ bool plan_split(const SegList& segs, int t_begin, int t_end, int max_tiles, Spli
     bd::SplitWave& W = pl->wv[w];
     W.tile[0] = W.tile[1] = -1;
     for (int q = 0; q < bd::kSplitMaxGroups; ++q) W.slot[q][0] = W.slot[q][1] = -1;
-    // waves w and w + 4 share a SIMD: the lighter one copies (ties: wave w + 4)
-    W.copier = -1;
+    W.copier = nd == 2 ? w : -1;
     W.pad_ = 0;
   }
-  for (int sm = 0; sm < 4; ++sm)
-    pl->wv[wave_load[sm] < wave_load[sm + 4] ? sm : sm + 4].copier = sm;
+  if (nd == 1) {
+    int wave_load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < nunits; ++k) wave_load[wave_of[k]] = units[k].cost;
+    // waves w and w + 4 share a SIMD: the lighter one copies (ties: wave w + 4)
+    for (int sm = 0; sm < 4; ++sm)
+      pl->wv[wave_load[sm] < wave_load[sm + 4] ? sm : sm + 4].copier = sm;
+  }
   for (int k = 0; k < nunits; ++k) {
     bd::SplitWave& W = pl->wv[wave_of[k]];
     const Unit& u = units[k];

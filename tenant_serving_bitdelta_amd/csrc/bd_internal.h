@@ -211,7 +211,8 @@ struct SplitProblem {
 struct SplitWave {
   int32_t tile[2];                       // 16-token block (relative) of the dense tiles, -1 none
   int32_t slot[kSplitMaxGroups][2];      // slot group g: the variant slot of tile i's pair, -1 none
-  int32_t copier;                        // 0..3: this wave issues copy share `copier`, -1 none
+  int32_t copier;                        // this wave issues copy share `copier` (0..7 with two
+                                         // tiles per wave, 0..3 with one), -1 none
   int32_t pad_;
 };
 

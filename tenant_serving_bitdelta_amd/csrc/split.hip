@@ -66,7 +66,9 @@ constexpr int kKS = 128;                 // k per step
 constexpr unsigned kWStage = kRows * kKS * 2;        // 32 KiB of W_base per step
 constexpr unsigned kSSlot = kRows * 16;              // one variant's sign words, one step: 2 KiB
 constexpr unsigned kLdsCap = 160 * 1024;             // LDS of one compute unit
-constexpr int kCopyWaves = 4;                        // waves that issue the global->LDS copies
+// waves that issue the global->LDS copies: all 8 with two dense tiles per wave; with one, the
+// less loaded wave of each SIMD (often one without a tile)
+constexpr int copy_waves(int nd) { return nd == 2 ? 8 : 4; }
 // per-row scales of a block, fp32, one run of kRows + 4 floats per variant slot (the padding
 // puts the runs of different slots on different LDS banks)
 constexpr int kRScaleStride = kRows + 4;
@@ -186,36 +188,41 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   const int j = lane & 15, g = lane >> 4;
 
   // ---- direct copies (global -> LDS), `ahead` steps ahead, into stage s % nst ------------------
-  // Four waves (the host picks the less loaded wave of each SIMD) issue every copy, 16 each per
-  // step, spread over their sign phase, so that the other wave of each SIMD is never held up by
-  // a full memory-instruction queue.
-  // W_base: copy b = 8*wave + u (of 32) moves rows 4b..4b+3 of the block for one step, 256 bytes
+  // The copying waves (copy share cw, from the host) issue kCopies copies each per step, spread
+  // over their sign phase.  With two tiles per wave every wave copies: with 4 waves issuing 16
+  // copies each, those waves took a tenth of a step longer than the others, which then waited
+  // at the barrier.
+  // W_base: copy b = kWCopies*cw + u (of 32) moves rows 4b..4b+3 of the block for one step, 256 bytes
   // each, so every 4 consecutive lanes read 64 contiguous bytes.  Lane L writes LDS slot
   // (row 4b + L/16, 16-byte position L%16) and fetches 16-byte column chunk position ^ (row%16):
   // the XOR swizzle keeps the MFMA operand reads below conflict-free.
   const int cw_raw = a.wv[wave].copier;
   const bool copier = cw_raw >= 0;
   const int cw = copier ? cw_raw : 0;
+  constexpr int kCopyWaves = copy_waves(ND);
+  constexpr int kWCopies = 32 / kCopyWaves;  // W_base copies per copying wave and step
+  constexpr int kCopies = 2 * kWCopies;      // all copies per copying wave and step
   const rsrc_t wrs = make_rsrc(P.w + (size_t)row0 * d_in);
-  unsigned woff[8];
+  unsigned woff[kWCopies];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int rl = 4 * (8 * cw + u) + (lane >> 4);
+  for (int u = 0; u < kWCopies; ++u) {
+    const int rl = 4 * (kWCopies * cw + u) + (lane >> 4);
     const int row = min(row0 + rl, d_out - 1) - row0;
     woff[u] = (unsigned)((row * d_in + 8 * ((lane & 15) ^ (rl & 15))) * 2);
   }
   // sign words (tiled layout): the 128 rows of this block for one step are 2 KiB contiguous at
-  // word (rb * nsteps + s) * 512.  Copy q = wave + 4u moves half q % 2 of slot q / 2.
-  const unsigned soff = (unsigned)rb * (unsigned)nsteps * 2048u + (unsigned)(cw & 1) * 1024u +
-                        (unsigned)lane * 16u;
-  // copy k (< 16) of this wave for step s into the stage at byte st
+  // word (rb * nsteps + s) * 512; share cw moves both 1 KiB halves of slots cw,
+  // cw + kCopyWaves, ...
+  const unsigned soff = (unsigned)rb * (unsigned)nsteps * 2048u + (unsigned)lane * 16u;
+  // copy k (< kCopies) of this wave for step s into the stage at byte st
   auto copy = [&](int k, int s, unsigned st) {
-    if (k < 8) {
-      dma16(wrs, woff[k] + (unsigned)s * (kKS * 2), smem + st + (8 * cw + k) * 1024);
+    if (k < kWCopies) {
+      dma16(wrs, woff[k] + (unsigned)s * (kKS * 2), smem + st + (kWCopies * cw + k) * 1024);
     } else {
-      const int q = cw + kCopyWaves * (k - 8);
+      const int j = k - kWCopies;
+      const int q = 2 * (cw + kCopyWaves * (j >> 1)) + (j & 1);
       if (q < 2 * nslots)
-        dma16(make_rsrc(P.words[q >> 1]), soff + (unsigned)s * 2048u,
+        dma16(make_rsrc(P.words[q >> 1]), soff + (unsigned)(j & 1) * 1024u + (unsigned)s * 2048u,
               smem + st + kWStage + q * 1024);
     }
   };
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   if (copier)
     for (int r = 0; r < ahead && k0 + r < k1; ++r)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) copy(k, k0 + r, (unsigned)r * stage_bytes);
+      for (int k = 0; k < kCopies; ++k) copy(k, k0 + r, (unsigned)r * stage_bytes);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < ND; ++i) load_xq(i, (unsigned)k0);
@@ -334,8 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   const unsigned ring = (unsigned)nst * stage_bytes;
   // sign sum over this wave's slot groups, into the dense tiles.  The fp4 operands of a group's
   // variant are expanded once for both of its tiles; each pair issues its 8 hi-term MFMAs before
-  // its 8 lo-term MFMAs, so dependent MFMAs are 8 apart.  With copies, the wave issues 16 / NG of
-  // its copies of step cs before each group.
+  // its 8 lo-term MFMAs, so dependent MFMAs are 8 apart.  With copies, the wave issues
+  // kCopies / NG of its copies of step cs before each group.
   u32x4 S[kRT];
   // Lanes whose token is not of the pair's variant get block scale 2^-127 for both terms, so
   // their products vanish below fp32 resolution (at most 2^-120 in magnitude per product).
@@ -392,10 +399,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 #pragma unroll
         for (int qq = 0; qq < NG; ++qq) {
           if (copies) {
-            constexpr int kPer = 16 / (ND * NG);
             const int it = i * NG + qq;
 #pragma unroll
-            for (int k = it * kPer; k < (it + 1) * kPer; ++k) copy(k, cs, cst);
+            for (int k = it * kCopies / (ND * NG); k < (it + 1) * kCopies / (ND * NG); ++k)
+              copy(k, cs, cst);
           }
           const int q = i == 0 ? NG - 1 - qq : qq;
           const int sl = gslot[q][i];
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
     for (int q = 0; q < NG; ++q) {
       if (copies) {
 #pragma unroll
-        for (int k = q * (16 / NG); k < (q + 1) * (16 / NG); ++k) copy(k, cs, cst);
+        for (int k = q * (kCopies / NG); k < (q + 1) * (kCopies / NG); ++k) copy(k, cs, cst);
       }
       const int s0 = gslot[q][0];
       if (s0 >= 0) {
@@ -852,7 +859,7 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
   unsigned copy_shares = 0;
   for (int w = 0; w < kWaves; ++w) {
     const SplitWave& W = a.wv[w];
-    if (W.copier < -1 || W.copier >= kCopyWaves) return hipErrorInvalidValue;
+    if (W.copier < -1 || W.copier >= copy_waves(nd)) return hipErrorInvalidValue;
     if (W.copier >= 0) {
       if (copy_shares >> W.copier & 1u) return hipErrorInvalidValue;
       copy_shares |= 1u << W.copier;
@@ -866,7 +873,7 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
         if (slot >= 0 && (q >= ng || i >= nd || W.tile[i] < 0)) return hipErrorInvalidValue;
       }
   }
-  if (copy_shares != (1u << kCopyWaves) - 1u) return hipErrorInvalidValue;  // every copy issued
+  if (copy_shares != (1u << copy_waves(nd)) - 1u) return hipErrorInvalidValue;  // every copy issued
   // variants with one scale per output row: with two tiles per wave their scales take
   // kRowScaleBytes of LDS past the ring
   bool rows = false;

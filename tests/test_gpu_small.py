@@ -244,6 +244,8 @@ PATH_CASES = [
     ("m600", 136, 384, 600, 3, 0.1, ("prefill", "stream", "split")),
     ("m40-base-only", 80, 256, 40, 2, 1.0, ("stream", "split", "prefill")),
     ("m200-62v-chunks", 66, 384, 200, 62, 0.0, ("split", "stream")),
+    # whole 256 x 256 prefill tiles beside partial ones, an odd number of 32-wide K steps
+    ("m600-full-tiles", 520, 2080, 600, 2, 0.0, ("prefill",)),
 ]
 
 
@@ -292,6 +294,24 @@ def test_identity_readback_exact():
             continue
         want = want_bf16 if path == "prefill" else want_f32
         np.testing.assert_array_equal(got, want.astype(np.float32), err_msg=path)
+
+
+@pytest.mark.parametrize("d_out,d_in", [(512, 256), (320, 288)])
+def test_prefill_readback_exact_full_tiles(d_out, d_in):
+    """x = I on the prefill path with whole 256-token, 256-row tiles (and, for d_in = 288, an
+    odd number of K steps and partial tiles beside them): every weight of W_eff comes back as
+    bf16(fp32(w + alpha*s)), bit for bit."""
+    rng = np.random.default_rng(23)
+    w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
+    delta = rng.laplace(0, 3e-4, size=(d_out, d_in)).astype(np.float32)
+    x_bits = WL.f32_to_bf16_bits(np.eye(d_in, dtype=np.float32))
+    (words, alpha, tiled), = gpu_compress([delta])
+    ref_words, ref_alpha = O.compress_ref(delta)
+    weff = O.reconstruct_ref(O.bf16_bits_to_f64(w_bits), ref_words, ref_alpha)  # fp64 exact
+    want = O.bf16_bits_to_f64(WL.f32_to_bf16_bits(weff.astype(np.float32))).T
+    y = bd.matmul(bf16_dev(x_bits), bf16_dev(w_bits), [(words, alpha, tiled)], [0, d_in], [0],
+                  out_dtype="f32", path="prefill")
+    np.testing.assert_array_equal(y.cpu().numpy(), want.astype(np.float32))
 
 
 def test_gemv_readback_exact():
