@@ -715,7 +715,8 @@ def _sub(r):
 
 def measure_copy_ceiling(torch, reps=5):
     """Device-to-device copy of a 2 GiB buffer (hipMemcpyAsync): bytes read + written per second,
-    the bandwidth a plain copy reaches on this GPU."""
+    the bandwidth a plain copy reaches on this GPU; and a read-only stream (row sums over 4 GiB).
+    The larger of the two is the measured ceiling."""
     n = 2 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -729,24 +730,25 @@ def measure_copy_ceiling(torch, reps=5):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     copy_gbs = 2 * n / (ms / 1e3) / 1e9
-    # read-only: a sum over 4 GiB of float32 (torch's reduction kernel), the kind of stream the
+    # read-only: row sums over 4 GiB of float32 (rows of 1024, torch's reduction kernel; a
+    # single sum of the whole tensor streams at about 4 TB/s only), the kind of stream the
     # read-dominated kernels here are (a copy also writes as many bytes as it reads)
     x = src.view(torch.float32)
     del dst
-    big = torch.cat([x, x])
+    big = torch.cat([x, x]).view(-1, 1024)
     del src, x
-    big.sum()
+    big.sum(dim=1)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        big.sum()
+        big.sum(dim=1)
     e1.record()
     torch.cuda.synchronize()
     rms = e0.elapsed_time(e1) / reps
     read_gbs = big.numel() * 4 / (rms / 1e3) / 1e9
     del big
-    return {"what": "device-to-device copy of 2 GiB (hipMemcpyAsync), read + write bytes; and a "
-                    "float32 sum over 4 GiB (read only)",
+    return {"what": "device-to-device copy of 2 GiB (hipMemcpyAsync), read + write bytes; and "
+                    "float32 row sums over 4 GiB (read only)",
             "copy_gbs": copy_gbs, "read_gbs": read_gbs, "gbs": max(copy_gbs, read_gbs), "ms": ms}
 
 
