@@ -134,6 +134,8 @@ bool split_eligible(const bitdelta_problem* probs, int np, int64_t M, const SegL
     if (P.d_in % 128 != 0) return false;
     if ((M + 15) / 16 * 16 * 2 * P.d_in >= (int64_t(1) << 31)) return false;
     if ((P.d_out + 127) / 128 * 128 * (P.d_in / 8) >= (int64_t(1) << 31)) return false;
+    // the schedule numbers row blocks and list entries in 16 bits
+    if ((P.d_out + 127) / 128 > 8192) return false;
     for (const Segment& s : segs) {
       if (s.variant < 0) continue;
       const uint32_t* t = P.variants[s.variant].sign_words_t128;
@@ -485,7 +487,8 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, cons
       sh.C = C;
       sh.Mp = Mp;
       sh.nslots = a.nslots;
-      sh.slots_avail = std::min(slots_total, bd::kMaxProblems * bd::kSplitSlotsPerLinear) / 8;
+      // partial slots (and split counters) per XCD: an eighth of the launch's linears' share
+      sh.slots_avail = std::min(slots_total, pn * bd::kSplitSlotsPerLinear) / 8;
       for (int q = 0; q < pn; ++q) {
         const bitdelta_problem& P = probs[order[p0 + q]];
         sh.ns[q] = (int)(P.d_in / 128);
@@ -498,7 +501,8 @@ bitdelta_status run_split(const bitdelta_problem* probs, int np, int64_t M, cons
       H.counter = counter;
       H.stats = stats;
       act.counter = counter;
-      act.ncounter = 8 * H.nsplit;
+      act.ncounter = 0;
+      for (int x = 0; x < 8; ++x) act.ncounter += H.x[x].nsplit;
       for (int q = 0; q < pn; ++q) {
         const int p = order[p0 + q];
         const bitdelta_problem& P = probs[p];

@@ -216,54 +216,96 @@ struct SplitWave {
   int32_t pad_;
 };
 
-// Work schedule of a split launch, the same for each of the 8 XCDs (XCD x serves the x-th eighth
-// of every linear's 128-row blocks, its "units"; units are counted with the largest eighth,
-// ceil(nblocks / 8)).  The grid's per-XCD list first holds one piece per unit, linear by linear:
-// steps [0, head) of each of its first units, all but the last `pooled` ones.  Then the pool:
-// linear by linear, the steps [head, nsteps) of its cut units (head < nsteps) in pieces of
-// `sigma` steps, then its pooled units whole, also in pieces of `sigma` steps; pieces of the
-// same steps of different units come one after another, so they run side by side and share
-// the activations in L2.  A unit done in several pieces is "split": each piece leaves its fp32
-// sums in a partial slot, and the piece that finishes last adds the slots in piece order and
-// writes y.  A split unit's counter (64 bits) holds in bits 0..7 the pieces counted in and in
-// bits 8 + 6x .. 13 + 6x the pieces that ran on XCD x.
+// Work schedule of a split launch.  The 128-row blocks of the launch's linears, in launch order,
+// are cut into 8 runs of about equal work (blocks times K steps), one per XCD, so that each
+// linear's blocks, and the activations they multiply, are served by as few XCDs as the balance
+// allows.  XCD x serves blocks first[q] .. first[q] + cnt[q] - 1 of linear q (its "units") and
+// walks one list: first one piece per unit, linear by linear: steps [0, min(cut, ns)) of each of
+// its units but the last `pooled` units of its last linear.  Then the pool: linear by linear, the
+// steps [head, ns) of its cut units (head = min(cut, ns) < ns) in pieces of `sigma` steps, then
+// its pooled units whole, also in pieces of `sigma` steps; pieces of the same steps of different
+// units come one after another, so they run side by side and share the activations in L2.  A
+// unit done in several pieces is "split": each piece leaves its fp32 sums in a partial slot, and
+// the piece that finishes last adds the slots in piece order and writes y.  A split unit's counter
+// (64 bits) holds in bits 0..7 the pieces counted in and in bits 8 + 6x .. 13 + 6x the pieces that
+// ran on XCD x.  The XCD's split units use counters split0 .., its partial slots slot0 ...
+struct SplitXcd {
+  int16_t first[kMaxProblems];           // first row block of linear q this XCD serves
+  int16_t cnt[kMaxProblems];             // row blocks of linear q it serves (0: none)
+  int16_t cut;                           // steps of a unit's first piece (at most ns)
+  int16_t pooled;                        // trailing units of its last linear done in the pool
+  int16_t sigma;                         // pool piece length in K steps (>= 1)
+  int16_t nheads, npool;                 // list lengths
+  int16_t nsplit, nslot;                 // split units and partial slots
+  int16_t split0, slot0;                 // its first split counter and first partial slot
+  int16_t pad_;
+};
 struct SplitSched {
-  int32_t head[kMaxProblems];            // steps of the first piece of every unit of linear q
-  int32_t pooled[kMaxProblems];          // trailing units of linear q done in the pool
-  int32_t sigma;                         // pool piece length in K steps (>= 1)
-  int32_t nheads, npool;                 // list lengths per XCD
-  int32_t nsplit, nslot;                 // split units and partial slots per XCD
+  SplitXcd x[8];
   uint32_t slot_bytes;                   // bytes of one partial slot (128 rows x 4 x Mp)
-  float* partial;                        // [8][nslot] partial slots
-  uint64_t* counter;                     // [8][nsplit] finished pieces per split unit
+  int32_t pad_;
+  float* partial;                        // partial slots of all XCDs
+  uint64_t* counter;                     // finished pieces per split unit, all XCDs
   uint32_t* stats;                       // [0]: handoffs whose pieces ran on several XCDs
 };
 
-// Piece kk of an XCD's list under schedule H, for linears with ns[q] K steps and nb[q] row
-// blocks (q < nprob): linear p (-1 past the end), unit lrb of the XCD's eighth, K steps [k0, k1);
-// for a split unit (nparts > 1) its piece index, split counter sid and first partial slot.
+// The lists' counts of an XCD under its parameters, for linears with ns[q] K steps (q < nprob);
+// returns the largest number of pieces of one unit.
+__host__ __device__ inline int split_xcd_counts(const SplitXcd& X, int nprob, const int* ns,
+                                                int* nheads, int* npool, int* nsplit, int* nslot) {
+  int last = -1;
+  for (int q = 0; q < nprob; ++q)
+    if (X.cnt[q] > 0) last = q;
+  int max_parts = 1;
+  *nheads = *npool = *nsplit = *nslot = 0;
+  for (int q = 0; q < nprob; ++q) {
+    if (X.cnt[q] <= 0) continue;
+    const int pooled = q == last ? X.pooled : 0;
+    const int head = X.cut < ns[q] ? X.cut : ns[q];
+    const int nh = X.cnt[q] - pooled, tail = ns[q] - head;
+    const int tp = tail > 0 ? (tail + X.sigma - 1) / X.sigma : 0;
+    const int pp = (ns[q] + X.sigma - 1) / X.sigma;
+    const int ncut = tail > 0 ? nh : 0;
+    *nheads += nh;
+    *npool += ncut * tp + pooled * pp;
+    *nsplit += ncut + pooled;
+    *nslot += ncut * (1 + tp) + pooled * pp;
+    if (ncut > 0 && 1 + tp > max_parts) max_parts = 1 + tp;
+    if (pooled > 0 && pp > max_parts) max_parts = pp;
+  }
+  return max_parts;
+}
+
+// Piece kk of XCD X's list, for linears with ns[q] K steps (q < nprob): linear p (-1 past the
+// end), row block rb, K steps [k0, k1); for a split unit (nparts > 1) its piece index, its split
+// counter sid and its first partial slot slot0 (both counted over all XCDs).
 struct SplitPiece {
-  int p, lrb, k0, k1, nparts, part, sid, slot0;
+  int p, rb, k0, k1, nparts, part, sid, slot0;
 };
-__host__ __device__ inline SplitPiece split_piece(const SplitSched& H, int nprob, const int* ns,
-                                                  const int* nb, int kk) {
+__host__ __device__ inline SplitPiece split_piece(const SplitXcd& X, int nprob, const int* ns,
+                                                  int kk) {
   SplitPiece r = {-1, 0, 0, 0, 1, 0, 0, 0};
-  const bool in_pool = kk >= H.nheads;
-  if (in_pool) kk -= H.nheads;
-  int sid_base = 0, slot_base = 0;
+  const bool in_pool = kk >= X.nheads;
+  if (in_pool) kk -= X.nheads;
+  int last = -1;
+#pragma unroll
+  for (int q = 0; q < kMaxProblems; ++q)
+    if (q < nprob && X.cnt[q] > 0) last = q;
+  int sid_base = X.split0, slot_base = X.slot0;
 #pragma unroll
   for (int q = 0; q < kMaxProblems; ++q) {
-    if (q < nprob) {
-      const int cnt = (nb[q] + 7) >> 3;                  // units of the largest eighth
-      const int nh = cnt - H.pooled[q];                  // units with a head piece
-      const int tail = ns[q] - H.head[q];
-      const int tp = tail > 0 ? (tail + H.sigma - 1) / H.sigma : 0;  // pool pieces of a cut unit
-      const int pp = (ns[q] + H.sigma - 1) / H.sigma;                // pieces of a pooled unit
+    if (q < nprob && X.cnt[q] > 0) {
+      const int pooled = q == last ? X.pooled : 0;
+      const int head = X.cut < ns[q] ? X.cut : ns[q];
+      const int nh = X.cnt[q] - pooled;                  // units with a head piece
+      const int tail = ns[q] - head;
+      const int tp = tail > 0 ? (tail + X.sigma - 1) / X.sigma : 0;  // pool pieces of a cut unit
+      const int pp = (ns[q] + X.sigma - 1) / X.sigma;                // pieces of a pooled unit
       const int ncut = tail > 0 ? nh : 0;
       if (r.p < 0) {
         if (!in_pool) {
           if (kk < nh) {
-            r.p = q; r.lrb = kk; r.k0 = 0; r.k1 = H.head[q];
+            r.p = q; r.rb = X.first[q] + kk; r.k0 = 0; r.k1 = head;
             if (tail > 0) {
               r.nparts = 1 + tp; r.part = 0; r.sid = sid_base + kk; r.slot0 = slot_base + kk * r.nparts;
             }
@@ -272,24 +314,24 @@ __host__ __device__ inline SplitPiece split_piece(const SplitSched& H, int nprob
           }
         } else if (kk < ncut * tp) {  // same steps of the cut units one after another
           const int jj = kk / ncut, u = kk - jj * ncut;
-          r.p = q; r.lrb = u; r.k0 = H.head[q] + jj * H.sigma;
-          r.k1 = r.k0 + H.sigma < ns[q] ? r.k0 + H.sigma : ns[q];
+          r.p = q; r.rb = X.first[q] + u; r.k0 = head + jj * X.sigma;
+          r.k1 = r.k0 + X.sigma < ns[q] ? r.k0 + X.sigma : ns[q];
           r.nparts = 1 + tp; r.part = 1 + jj; r.sid = sid_base + u; r.slot0 = slot_base + u * r.nparts;
         } else {
           kk -= ncut * tp;
-          if (kk < H.pooled[q] * pp) {
-            const int jj = kk / H.pooled[q], u = kk - jj * H.pooled[q];
-            r.p = q; r.lrb = nh + u; r.k0 = jj * H.sigma;
-            r.k1 = r.k0 + H.sigma < ns[q] ? r.k0 + H.sigma : ns[q];
+          if (kk < pooled * pp) {
+            const int jj = kk / pooled, u = kk - jj * pooled;
+            r.p = q; r.rb = X.first[q] + nh + u; r.k0 = jj * X.sigma;
+            r.k1 = r.k0 + X.sigma < ns[q] ? r.k0 + X.sigma : ns[q];
             r.nparts = pp; r.part = jj; r.sid = sid_base + ncut + u;
             r.slot0 = slot_base + ncut * (1 + tp) + u * pp;
           } else {
-            kk -= H.pooled[q] * pp;
+            kk -= pooled * pp;
           }
         }
       }
-      sid_base += ncut + H.pooled[q];
-      slot_base += ncut * (1 + tp) + H.pooled[q] * pp;
+      sid_base += ncut + pooled;
+      slot_base += ncut * (1 + tp) + pooled * pp;
     }
   }
   return r;

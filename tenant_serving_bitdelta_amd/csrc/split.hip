@@ -157,25 +157,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
 
   // ---- which piece: linear, 128-row block and K steps (wave-uniform) ---------------------------
   // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), and each
-  // XCD takes its list (the schedule above) in order.  XCD x serves the x-th eighth of every
-  // linear's row blocks, so the workgroups that run side by side on one XCD (sharing its L2) read
-  // the same activations at the same time.
+  // XCD takes its list (the schedule above) in order: its run of the linears' row blocks, so
+  // that a linear's activations are fetched into few XCDs' L2, and the workgroups running side by
+  // side on one XCD read the same activations at the same time.
   const SplitSched& H = a.sch;
   const int xcd = blockIdx.x & 7;
-  int ns_q[kMaxProblems], nb_q[kMaxProblems];
+  int ns_q[kMaxProblems];
 #pragma unroll
-  for (int q = 0; q < kMaxProblems; ++q) {
-    ns_q[q] = q < a.nprob ? a.prob[q].d_in / kKS : 0;
-    nb_q[q] = q < a.nprob ? a.prob[q].nblocks : 0;
-  }
-  const SplitPiece pc0 = split_piece(H, a.nprob, ns_q, nb_q, (int)(blockIdx.x >> 3));
-  const int p = pc0.p, lrb = pc0.lrb, k0 = pc0.k0, k1 = pc0.k1, nparts = pc0.nparts,
+  for (int q = 0; q < kMaxProblems; ++q) ns_q[q] = q < a.nprob ? a.prob[q].d_in / kKS : 0;
+  const SplitPiece pc0 = split_piece(H.x[xcd], a.nprob, ns_q, (int)(blockIdx.x >> 3));
+  const int p = pc0.p, rb = pc0.rb, k0 = pc0.k0, k1 = pc0.k1, nparts = pc0.nparts,
             part = pc0.part, sid = pc0.sid, slot0 = pc0.slot0;
-  if (p < 0) return;  // past the end of the list
+  if (p < 0) return;  // past the end of this XCD's list
   const SplitProblem& P = a.prob[p];
-  const int rb_lo = (xcd * P.nblocks) >> 3;
-  if (lrb >= (((xcd + 1) * P.nblocks) >> 3) - rb_lo) return;  // this XCD's eighth is shorter
-  const int rb = rb_lo + lrb;
   const int d_in = P.d_in, d_out = P.d_out;
   const int row0 = rb * kRows;
   const int nslots = a.nslots;
@@ -556,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
   // device scope (invalidating stale lines of its L2) and counts the event in the stats word.
   if (nparts > 1) {
     const rsrc_t prs = make_rsrc(reinterpret_cast<unsigned char*>(H.partial) +
-                                 (size_t)(xcd * H.nslot + slot0) * H.slot_bytes);
+                                 (size_t)slot0 * H.slot_bytes);
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       if (!dreal[i]) continue;
@@ -576,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(const SplitArgs a, u
       const unsigned x = hw & 7u;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const unsigned long long old = __hip_atomic_fetch_add(
-          H.counter + xcd * H.nsplit + sid, 1ull + (1ull << (8 + 6 * x)), __ATOMIC_RELAXED,
+          H.counter + sid, 1ull + (1ull << (8 + 6 * x)), __ATOMIC_RELAXED,
           __HIP_MEMORY_SCOPE_AGENT);
       const bool last = (int)(old & 0xFFu) == nparts - 1;
       const bool elsewhere = ((old >> 8) & ~(0x3Full << (6 * x))) != 0ull;
@@ -890,34 +884,47 @@ hipError_t launch_split(const SplitArgs& a, int nd, int ng, hipStream_t stream) 
   int nst = lds / (int)stage;
   nst = nst > 4 ? 4 : nst;
   if (nst < 2) return hipErrorInvalidConfiguration;
-  // the schedule must describe the lists the kernel walks (see the piece map in the kernel)
+  // the schedule must describe the lists the kernel walks (see the piece map in the kernel): each
+  // linear's row blocks tiled by the XCDs' runs in XCD order, every list's counts as its
+  // parameters give them, counters and partial slots numbered XCD after XCD within what the
+  // workspace holds (kSplitSlotsPerLinear of each per linear)
   const SplitSched& H = a.sch;
-  if (H.sigma < 1) return hipErrorInvalidValue;
-  int nheads = 0, npool = 0, nsplit = 0, nslot = 0, max_parts = 1;
+  int ns[kMaxProblems], pos[kMaxProblems];
+  for (int q = 0; q < kMaxProblems; ++q) ns[q] = pos[q] = 0;
   for (int q = 0; q < a.nprob; ++q) {
     const SplitProblem& P = a.prob[q];
     if (P.nblocks < 1 || P.d_in < kKS || P.d_in % kKS != 0) return hipErrorInvalidValue;
-    const int ns = P.d_in / kKS, cnt = (P.nblocks + 7) >> 3;
-    if (H.head[q] < 1 || H.head[q] > ns || H.pooled[q] < 0 || H.pooled[q] > cnt)
-      return hipErrorInvalidValue;
-    const int nh = cnt - H.pooled[q], tail = ns - H.head[q];
-    const int tp = tail > 0 ? (tail + H.sigma - 1) / H.sigma : 0;
-    const int pp = (ns + H.sigma - 1) / H.sigma;
-    const int ncut = tail > 0 ? nh : 0;
-    nheads += nh;
-    npool += ncut * tp + H.pooled[q] * pp;
-    nsplit += ncut + H.pooled[q];
-    nslot += ncut * (1 + tp) + H.pooled[q] * pp;
-    if (ncut > 0) max_parts = max(max_parts, 1 + tp);
-    if (H.pooled[q] > 0) max_parts = max(max_parts, pp);
+    ns[q] = P.d_in / kKS;
   }
-  // a unit's counter has 6 bits per XCD field and 8 for the count
-  if (max_parts > 63) return hipErrorInvalidValue;
-  if (nheads != H.nheads || npool != H.npool || nsplit != H.nsplit || nslot != H.nslot)
+  int max_list = 0, split_end = 0, slot_end = 0;
+  for (int x = 0; x < 8; ++x) {
+    const SplitXcd& X = H.x[x];
+    if (X.sigma < 1 || X.cut < 1 || X.pooled < 0) return hipErrorInvalidValue;
+    for (int q = 0; q < kMaxProblems; ++q) {
+      if (X.cnt[q] < 0 || (q >= a.nprob && X.cnt[q] != 0)) return hipErrorInvalidValue;
+      if (X.cnt[q] > 0) {
+        if (X.first[q] != pos[q]) return hipErrorInvalidValue;
+        pos[q] += X.cnt[q];
+      }
+    }
+    int nh, npl, nsp, nsl;
+    const int max_parts = split_xcd_counts(X, a.nprob, ns, &nh, &npl, &nsp, &nsl);
+    // a unit's counter has 6 bits per XCD field and 8 for the count
+    if (max_parts > 63) return hipErrorInvalidValue;
+    if (nh != X.nheads || npl != X.npool || nsp != X.nsplit || nsl != X.nslot)
+      return hipErrorInvalidValue;
+    if (X.split0 != split_end || X.slot0 != slot_end) return hipErrorInvalidValue;
+    split_end += nsp;
+    slot_end += nsl;
+    max_list = max(max_list, nh + npl);
+  }
+  for (int q = 0; q < a.nprob; ++q)
+    if (pos[q] != a.prob[q].nblocks) return hipErrorInvalidValue;
+  if (split_end > a.nprob * kSplitSlotsPerLinear || slot_end > a.nprob * kSplitSlotsPerLinear)
     return hipErrorInvalidValue;
-  if (nslot > 0 && (!H.partial || !H.counter || !H.stats || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
+  if (slot_end > 0 && (!H.partial || !H.counter || !H.stats || H.slot_bytes < (unsigned)a.Mp * kRows * 4))
     return hipErrorInvalidValue;
-  const int nblocks = 8 * (nheads + npool);
+  const int nblocks = 8 * max_list;
   if (rows) {
     if (nd == 1) {
       if (ng <= 1) return launch_nd_ng<1, 1, kRowsAcc>(a, nblocks, stage, nst, stream);

@@ -1,8 +1,10 @@
-// Host check of the split decode schedule: for seeded random launch shapes, the piece lists the
-// kernel walks (split_piece) under the chosen schedule cover every (linear, row block, K step)
-// of every XCD exactly once, split units have consistent piece counts and in-range partial
-// slots and counters, the workspace's slot budget holds, and the simulated makespan is never
-// worse than running whole units.  Prints "ok" and exits 0 when every case passes.
+// Host check of the split decode schedule: for seeded random launch shapes, the XCDs' runs tile
+// each linear's row blocks in XCD order with about an eighth of the work each, the piece lists
+// the kernel walks (split_piece) under the chosen schedule cover every (linear, row block, K
+// step) exactly once, split units keep all their pieces on one XCD with consistent piece counts
+// and in-range partial slots and counters numbered XCD after XCD, the workspace's slot budget
+// holds, and the simulated makespan is never worse than running whole units.  Prints "ok" and
+// exits 0 when every case passes.
 #include <stdio.h>
 #include <string.h>
 
@@ -21,54 +23,100 @@ static int rnd(int n) {
   return (int)((g_seed >> 8) % (unsigned)n);
 }
 
+// whole units on every XCD's run (no cut, no pool), for comparison
+static SplitSched whole_units(const SplitShape& sh, const SplitSched& h) {
+  SplitSched w = h;
+  int split0 = 0, slot0 = 0;
+  for (int x = 0; x < 8; ++x) {
+    bd::SplitXcd& X = w.x[x];
+    int max_ns = 1;
+    for (int q = 0; q < sh.np; ++q)
+      if (X.cnt[q] > 0 && sh.ns[q] > max_ns) max_ns = sh.ns[q];
+    X.cut = (int16_t)max_ns;
+    X.sigma = (int16_t)max_ns;
+    X.pooled = 0;
+    int nh, npl, nsp, nsl;
+    bd::split_xcd_counts(X, sh.np, sh.ns, &nh, &npl, &nsp, &nsl);
+    X.nheads = (int16_t)nh; X.npool = (int16_t)npl; X.nsplit = (int16_t)nsp; X.nslot = (int16_t)nsl;
+    X.split0 = (int16_t)split0; X.slot0 = (int16_t)slot0;
+    split0 += nsp; slot0 += nsl;
+  }
+  return w;
+}
+
 static int check(const SplitShape& sh, const SplitSched& h) {
   int bad = 0;
-  if (h.nslot > sh.slots_avail) { printf("slot budget exceeded\n"); ++bad; }
+  std::map<std::tuple<int, int, int>, int> cover;
+  std::map<int, std::pair<int, int>> split_info;  // sid -> (nparts, first slot)
+  std::map<int, int> split_xcd;                   // sid -> the XCD whose list holds it
+  std::map<int, int> slot_use;
+  int split_end = 0, slot_end = 0;
+  int64_t total = 0, max_ns = 1;
+  for (int q = 0; q < sh.np; ++q) {
+    total += (int64_t)sh.nb[q] * sh.ns[q];
+    if (sh.ns[q] > max_ns) max_ns = sh.ns[q];
+  }
+  int pos[bd::kMaxProblems] = {0};
   for (int xcd = 0; xcd < 8; ++xcd) {
-    std::map<std::tuple<int, int, int>, int> cover;
-    std::map<int, std::pair<int, int>> split_info;
-    std::map<int, int> slot_use;
-    for (int kk = 0; kk < h.nheads + h.npool; ++kk) {
-      const SplitPiece pc = bd::split_piece(h, sh.np, sh.ns, sh.nb, kk);
+    const bd::SplitXcd& X = h.x[xcd];
+    if (X.nslot > sh.slots_avail || X.nsplit > sh.slots_avail) { printf("slot budget exceeded\n"); ++bad; }
+    if (X.split0 != split_end || X.slot0 != slot_end) { printf("counters or slots not numbered XCD after XCD\n"); ++bad; }
+    split_end += X.nsplit;
+    slot_end += X.nslot;
+    int nh, npl, nsp, nsl;
+    bd::split_xcd_counts(X, sh.np, sh.ns, &nh, &npl, &nsp, &nsl);
+    if (nh != X.nheads || npl != X.npool || nsp != X.nsplit || nsl != X.nslot) { printf("list counts differ\n"); ++bad; }
+    // runs: each linear's blocks tiled by the XCDs in order; the XCD's work near an eighth
+    int64_t work = 0;
+    for (int q = 0; q < sh.np; ++q) {
+      if (X.cnt[q] > 0) {
+        if (X.first[q] != pos[q]) { printf("xcd %d linear %d run starts at %d, not %d\n", xcd, q, X.first[q], pos[q]); ++bad; }
+        pos[q] += X.cnt[q];
+      }
+      work += (int64_t)X.cnt[q] * sh.ns[q];
+    }
+    if (8 * work > total + 8 * max_ns || 8 * work < total - 8 * max_ns) {
+      printf("xcd %d has %lld of %lld steps\n", xcd, (long long)work, (long long)total);
+      ++bad;
+    }
+    for (int kk = 0; kk < X.nheads + X.npool; ++kk) {
+      const SplitPiece pc = bd::split_piece(X, sh.np, sh.ns, kk);
       if (pc.p < 0) { printf("piece %d of the list maps to nothing\n", kk); ++bad; continue; }
-      const int lo = (xcd * sh.nb[pc.p]) >> 3, len = (((xcd + 1) * sh.nb[pc.p]) >> 3) - lo;
-      if (pc.lrb >= len) continue;  // this XCD's eighth is shorter
+      if (pc.rb < X.first[pc.p] || pc.rb >= X.first[pc.p] + X.cnt[pc.p]) { printf("block outside the XCD's run\n"); ++bad; }
       if (!(0 <= pc.k0 && pc.k0 < pc.k1 && pc.k1 <= sh.ns[pc.p])) { printf("bad K range\n"); ++bad; }
-      for (int s = pc.k0; s < pc.k1; ++s) cover[std::make_tuple(pc.p, lo + pc.lrb, s)]++;
+      for (int s = pc.k0; s < pc.k1; ++s) cover[std::make_tuple(pc.p, pc.rb, s)]++;
       if (pc.nparts > 1) {
-        if (pc.sid < 0 || pc.sid >= h.nsplit || pc.part < 0 || pc.part >= pc.nparts ||
-            pc.slot0 < 0 || pc.slot0 + pc.part >= h.nslot) { printf("split index out of range\n"); ++bad; }
+        if (pc.sid < X.split0 || pc.sid >= X.split0 + X.nsplit || pc.part < 0 || pc.part >= pc.nparts ||
+            pc.slot0 < X.slot0 || pc.slot0 + pc.part >= X.slot0 + X.nslot) { printf("split index out of range\n"); ++bad; }
         auto it = split_info.find(pc.sid);
         if (it == split_info.end()) split_info[pc.sid] = std::make_pair(pc.nparts, pc.slot0);
         else if (it->second != std::make_pair(pc.nparts, pc.slot0)) { printf("inconsistent split unit\n"); ++bad; }
+        auto ix = split_xcd.find(pc.sid);
+        if (ix == split_xcd.end()) split_xcd[pc.sid] = xcd;
+        else if (ix->second != xcd) { printf("split unit %d on two XCDs\n", pc.sid); ++bad; }
         if (slot_use[pc.slot0 + pc.part]++) { printf("partial slot used twice\n"); ++bad; }
       }
     }
-    // every split unit gets all its pieces on this XCD
-    for (const auto& e : split_info) {
-      int n = 0;
-      for (int k = 0; k < e.second.first; ++k) n += slot_use.count(e.second.second + k) ? 1 : 0;
-      if (n != e.second.first) { printf("split unit %d has %d of %d pieces\n", e.first, n, e.second.first); ++bad; }
-    }
-    for (int q = 0; q < sh.np; ++q) {
-      const int lo = (xcd * sh.nb[q]) >> 3, len = (((xcd + 1) * sh.nb[q]) >> 3) - lo;
-      for (int r = lo; r < lo + len; ++r)
-        for (int s = 0; s < sh.ns[q]; ++s)
-          if (cover[std::make_tuple(q, r, s)] != 1) {
-            if (bad < 8) printf("xcd %d linear %d block %d step %d covered %d times\n", xcd, q, r, s,
-                                cover[std::make_tuple(q, r, s)]);
-            ++bad;
-          }
-    }
   }
-  SplitSched whole;
-  memset(&whole, 0, sizeof(whole));
-  int max_ns = 1;
-  for (int q = 0; q < sh.np; ++q) { whole.head[q] = sh.ns[q]; if (sh.ns[q] > max_ns) max_ns = sh.ns[q]; }
-  whole.sigma = max_ns;
-  whole.nheads = 0;
-  for (int q = 0; q < sh.np; ++q) whole.nheads += (sh.nb[q] + 7) >> 3;
-  if (bd::split_schedule_makespan(sh, h) > bd::split_schedule_makespan(sh, whole) + 1e-9) {
+  if (split_end > sh.slots_avail * 8 || slot_end > sh.slots_avail * 8) { printf("workspace exceeded\n"); ++bad; }
+  // every split unit gets all its pieces
+  for (const auto& e : split_info) {
+    int n = 0;
+    for (int k = 0; k < e.second.first; ++k) n += slot_use.count(e.second.second + k) ? 1 : 0;
+    if (n != e.second.first) { printf("split unit %d has %d of %d pieces\n", e.first, n, e.second.first); ++bad; }
+  }
+  // every (linear, block, step) exactly once
+  for (int q = 0; q < sh.np; ++q) {
+    if (pos[q] != sh.nb[q]) { printf("linear %d: runs cover %d of %d blocks\n", q, pos[q], sh.nb[q]); ++bad; }
+    for (int r = 0; r < sh.nb[q]; ++r)
+      for (int s = 0; s < sh.ns[q]; ++s)
+        if (cover[std::make_tuple(q, r, s)] != 1) {
+          if (bad < 8) printf("linear %d block %d step %d covered %d times\n", q, r, s,
+                              cover[std::make_tuple(q, r, s)]);
+          ++bad;
+        }
+  }
+  if (bd::split_schedule_makespan(sh, h) > bd::split_schedule_makespan(sh, whole_units(sh, h)) + 1e-9) {
     printf("schedule slower than whole units\n");
     ++bad;
   }
@@ -93,13 +141,7 @@ int main() {
       // whole units leave a tail here (the 224-step down blocks and a last round of 64-step
       // blocks on few compute units; 204 steps per compute unit on average): the schedule must
       // end at least 10% sooner than whole units do in the same cost model
-      SplitSched w;
-      memset(&w, 0, sizeof(w));
-      for (int q = 0; q < sh.np; ++q) {
-        w.head[q] = sh.ns[q];
-        w.nheads += (sh.nb[q] + 7) >> 3;
-      }
-      w.sigma = 224;
+      const SplitSched w = whole_units(sh, h);
       const double t = bd::split_schedule_makespan(sh, h);
       const double tw = bd::split_schedule_makespan(sh, w);
       if (t > 0.9 * tw) {
