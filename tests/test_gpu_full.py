@@ -54,7 +54,8 @@ def test_full_size_block_sampled(config, m, dist):
             del dh
         y = torch.empty((m, d_out), dtype=torch.bfloat16, device="cuda")
         layers.append((name, d_out, d_in, w, x, y, variants, rows, ref))
-    ws = torch.empty(sum(bd.matmul_workspace_bytes(m, d_in, "auto") for _, _, d_in, *_ in layers),
+    # zeroed: its statistics word only ever grows (below: K-split handoffs across XCDs)
+    ws = torch.zeros(sum(bd.matmul_workspace_bytes(m, d_in, "auto") for _, _, d_in, *_ in layers),
                      dtype=torch.uint8, device="cuda")
     probs = [(x, w, y, variants) for _, _, _, w, x, y, variants, _, _ in layers]
     assert bd.auto_path(m, offs, segv) == bd.PATHS["split"]
@@ -63,6 +64,13 @@ def test_full_size_block_sampled(config, m, dist):
     bd.matmul_grouped([(x, w, yy, v) for (x, w, _, v), yy in zip(probs, y32)], offs, segv,
                       out_dtype="f32", workspace=ws)
     torch.cuda.synchronize()
+    # each XCD serves its own run of the block's row blocks, and every split unit's pieces are on
+    # one XCD's list: the first statistics block (past the activation parts, partial slots and
+    # counters of all seven linears) counts handoffs whose pieces ran on several XCDs
+    nstat = ws.numel() - len(layers) * 256
+    stats = ws[nstat:nstat + 4].view(torch.int32).item()
+    print(f"  split handoffs across XCDs: {stats}", flush=True)
+    assert stats == 0
 
     for (name, d_out, d_in, w, x, y, variants, rows, ref), yf in zip(layers, y32):
         wf = w[rows].float().cpu().numpy().astype(np.float64)
