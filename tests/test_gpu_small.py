@@ -544,6 +544,41 @@ def test_split_k_pieces_grouped():
         assert rel.max() <= 5e-3, f"row rel L2 {rel.max():.3e}"
 
 
+def test_split_xcd_runs_eight_linears():
+    """Eight linears of mixed shapes in one grouped launch (the most one launch takes): the row
+    blocks are cut into 8 runs of equal work, so runs start and end inside linears and some XCDs
+    serve several linears, each with its own cut and pool; every output matches the oracle and
+    no K-split handoff runs across XCDs (the statistics word, zeroed first, stays 0)."""
+    rng = np.random.default_rng(93)
+    m, nv = 40, 3
+    ids = rng.integers(-1, nv, size=m).astype(np.int32)
+    perm, offs, segv = bd.plan_segments(ids, nv)
+    shapes = [(64, 4096), (1000, 1024), (384, 2048), (130, 8192), (256, 512), (768, 1536),
+              (128, 6144), (520, 2560)]
+    probs, refs = [], []
+    for d_out, d_in in shapes:
+        w_bits = WL.f32_to_bf16_bits(rng.normal(0, 0.02, size=(d_out, d_in)).astype(np.float32))
+        deltas = [rng.laplace(0, 4e-4, size=(d_out, d_in)).astype(np.float32) for _ in range(nv)]
+        x_bits = WL.f32_to_bf16_bits(rng.normal(size=(m, d_in)).astype(np.float32))
+        var_gpu = gpu_compress(deltas)
+        y = torch.empty((m, d_out), dtype=torch.float32, device="cuda")
+        probs.append((bf16_dev(x_bits[perm]), bf16_dev(w_bits), y, var_gpu))
+        refs.append(O.matmul_ref(O.bf16_bits_to_f64(x_bits)[perm], O.bf16_bits_to_f64(w_bits),
+                                 [O.compress_ref(d) for d in deltas], offs, segv))
+    need = sum(bd.matmul_workspace_bytes(m, d_in, "split") for _, d_in in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        bd.matmul_grouped(probs, offs, segv, path="split", out_dtype="f32", workspace=ws)
+        torch.cuda.synchronize()
+        for (_, _, y, _), y_ref in zip(probs, refs):
+            rel = row_rel_l2(y.cpu().numpy().astype(np.float64), y_ref)
+            assert rel.max() <= 5e-3, f"row rel L2 {rel.max():.3e}"
+    nstat = need - len(shapes) * 256   # the first linear's statistics block
+    stats = ws[nstat:nstat + 4].view(torch.int32).item()
+    print(f"  split handoffs across XCDs: {stats}", flush=True)
+    assert stats == 0
+
+
 def test_split_k_pieces_meet_on_one_xcd():
     """The split K ranges of one row block are scheduled onto one XCD; the kernel checks the XCD
     each piece ran on (hardware register) and counts in the workspace's statistics word every
